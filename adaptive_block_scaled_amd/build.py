@@ -1,0 +1,76 @@
+"""Build libif4.so (HIP for gfx950) in-tree with hipcc.
+
+Flags:
+  --offload-arch=gfx950         MI355X only.
+  -ffp-contract=off             no implicit fma: every fused multiply-add in
+                                the kernels is written explicitly, so the
+                                fp32 error sums are exactly the ops stated.
+  -fno-gpu-flush-denormals-to-zero, -fhip-fp32-correctly-rounded-divide-sqrt
+                                IEEE fp32 (denormals kept, exact division).
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                no packed fp32 (v_pk_*_f32) code generation.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libif4.so")
+
+SOURCES = ["api.cpp", "quantize.hip", "dequantize.hip", "gemm.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+        if len(procs) >= jobs:
+            _wait(procs.pop(0))
+    while procs:
+        _wait(procs.pop(0))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _wait(item):
+    src, p = item
+    out, _ = p.communicate()
+    text = out.decode(errors="replace")
+    # hipcc's host pass does not know the packed-fp32 target feature; that
+    # warning is expected and harmless
+    lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
+    if p.returncode != 0:
+        sys.stderr.write("\n".join(lines) + "\n")
+        raise RuntimeError(f"hipcc failed on {src}")
+    if any(l.strip() for l in lines):
+        sys.stderr.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

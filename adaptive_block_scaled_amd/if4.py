@@ -1,0 +1,126 @@
+"""Thin Python binding of libif4 (include/if4.h).
+
+Argument marshalling only: device pointers, sizes and the current HIP stream
+cross the boundary; every step of quantize / dequantize / GEMM runs in the
+HIP kernels of libif4.so.  PyTorch is used for device memory and streams.
+There is no fallback: if the library is missing the import of this module
+raises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libif4.so")
+
+IF4_OK, IF4_ERR_NULL, IF4_ERR_SHAPE, IF4_ERR_ALIGN, IF4_ERR_DTYPE, IF4_ERR_RANGE, IF4_ERR_HIP = range(7)
+IF4_F32, IF4_BF16 = 0, 1
+MODE_ADAPTIVE, MODE_FORCE_FP4, MODE_FORCE_INT4 = 0, 1, 2
+GROUP = 16
+
+EXPORTS = ("if4_version", "if4_status_string", "if4_quantize", "if4_quantize_mode",
+           "if4_dequantize", "if4_gemm")
+
+
+class IF4Error(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libif4.so not found at {LIB_PATH}; build it with "
+            "`python -m adaptive_block_scaled_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    L.if4_version.restype = ci
+    L.if4_version.argtypes = []
+    L.if4_status_string.restype = ctypes.c_char_p
+    L.if4_status_string.argtypes = [ci]
+    L.if4_quantize.restype = ci
+    L.if4_quantize.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, vp]
+    L.if4_quantize_mode.restype = ci
+    L.if4_quantize_mode.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
+    L.if4_dequantize.restype = ci
+    L.if4_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, ci, i64, vp]
+    L.if4_gemm.restype = ci
+    L.if4_gemm.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.if4_status_string(status).decode()
+
+
+def version() -> int:
+    return lib.if4_version()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(fn, st):
+    if st != IF4_OK:
+        raise IF4Error(fn, st)
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return IF4_BF16
+    if dt == torch.float32:
+        return IF4_F32
+    raise TypeError(f"IF4 supports float32 and bfloat16 tensors, not {dt}")
+
+
+def quantize(x: torch.Tensor, scale_exp: int = 0, mode: int = MODE_ADAPTIVE, out=None):
+    """Quantize a 2-D [rows, cols] CUDA tensor (fp32 or bf16, unit stride
+    along dim 1) to IF4.  Returns (codes uint8 [rows, cols/2], scales uint8
+    [rows, cols/16]); `out` may pass preallocated (codes, scales)."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor with unit stride along dim 1")
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // GROUP), dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    st = lib.if4_quantize_mode(x.data_ptr(), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                               codes.data_ptr(), scales.data_ptr(), int(scale_exp), int(mode),
+                               _stream(x.device))
+    _check("if4_quantize_mode", st)
+    return codes, scales
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, scale_exp: int = 0,
+               dtype=torch.float32, out=None) -> torch.Tensor:
+    rows, half = codes.shape
+    cols = 2 * half
+    if scales.shape != (rows, cols // GROUP):
+        raise ValueError("scales must be [rows, cols/16]")
+    y = torch.empty((rows, cols), dtype=dtype, device=codes.device) if out is None else out
+    st = lib.if4_dequantize(codes.data_ptr(), scales.data_ptr(), rows, cols, int(scale_exp),
+                            y.data_ptr(), _dtype_code(y.dtype), y.stride(0),
+                            _stream(codes.device))
+    _check("if4_dequantize", st)
+    return y
+
+
+def gemm(a_codes, a_scales, a_exp, w_codes, w_scales, w_exp, out=None) -> torch.Tensor:
+    """C[M, N] = A[M, K] W[N, K]^T for IF4 operands; fp32 result."""
+    M, K = a_codes.shape[0], 2 * a_codes.shape[1]
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("A and W must share K")
+    c = torch.empty((M, N), dtype=torch.float32, device=a_codes.device) if out is None else out
+    st = lib.if4_gemm(a_codes.data_ptr(), a_scales.data_ptr(), int(a_exp), w_codes.data_ptr(),
+                      w_scales.data_ptr(), int(w_exp), M, N, K, c.data_ptr(), c.stride(0),
+                      _stream(a_codes.device))
+    _check("if4_gemm", st)
+    return c

@@ -1,0 +1,94 @@
+"""The C-ABI library: loads, exports every entry point include/if4.h
+declares, and rejects bad arguments on the host before any HIP call (so
+these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "if4.h")
+LIB = os.path.join(ROOT, "adaptive_block_scaled_amd", "libif4.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libif4.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(if4_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from adaptive_block_scaled_amd import if4
+    return if4.lib
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names == sorted(["if4_version", "if4_status_string", "if4_quantize",
+                            "if4_quantize_mode", "if4_dequantize", "if4_gemm"])
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.if4_version() >= 100
+    for st in range(7):
+        assert L.if4_status_string(st)
+    assert L.if4_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # 16-byte aligned fake device address; never dereferenced
+
+
+def q(L, x=FAKE, dt=1, rows=4, cols=32, ld=32, codes=FAKE, scales=FAKE, e=0, mode=0):
+    return L.if4_quantize_mode(x, dt, rows, cols, ld, codes, scales, e, mode, None)
+
+
+def test_quantize_validation(L):
+    assert q(L, dt=7) == 4
+    assert q(L, mode=3) == 4
+    assert q(L, cols=24, ld=24) == 2
+    assert q(L, rows=-1) == 2
+    assert q(L, ld=16) == 2
+    assert q(L, e=65) == 5 and q(L, e=-65) == 5
+    assert q(L, x=None) == 1 and q(L, codes=None) == 1 and q(L, scales=None) == 1
+    assert q(L, x=FAKE + 2) == 3
+    assert q(L, codes=FAKE + 4) == 3
+    assert q(L, dt=1, ld=36) == 3      # 72 B rows: not a multiple of 16
+    # empty inputs are valid and launch nothing
+    assert q(L, rows=0) == 0 and q(L, rows=3, cols=0, ld=0) == 0
+    assert L.if4_quantize(FAKE, 1, 0, 32, 32, FAKE, FAKE, 0, None) == 0
+
+
+def test_dequantize_validation(L):
+    d = L.if4_dequantize
+    assert d(FAKE, FAKE, 4, 32, 0, FAKE, 5, 32, None) == 4
+    assert d(FAKE, FAKE, 4, 20, 0, FAKE, 0, 32, None) == 2
+    assert d(FAKE, FAKE, 4, 32, 0, FAKE, 0, 16, None) == 2
+    assert d(FAKE, FAKE, 4, 32, 99, FAKE, 0, 32, None) == 5
+    assert d(None, FAKE, 4, 32, 0, FAKE, 0, 32, None) == 1
+    assert d(FAKE, FAKE, 4, 32, 0, FAKE + 8, 0, 32, None) == 3
+    assert d(FAKE, FAKE, 0, 32, 0, FAKE, 0, 32, None) == 0
+
+
+def test_gemm_validation(L):
+    g = L.if4_gemm
+    assert g(FAKE, FAKE, 0, FAKE, FAKE, 0, 8, 8, 24, FAKE, 8, None) == 2
+    assert g(FAKE, FAKE, 0, FAKE, FAKE, 0, 8, 8, 32, FAKE, 4, None) == 2
+    assert g(FAKE, FAKE, 0, FAKE, FAKE, 0, -1, 8, 32, FAKE, 8, None) == 2
+    assert g(FAKE, FAKE, 70, FAKE, FAKE, 0, 8, 8, 32, FAKE, 8, None) == 5
+    assert g(FAKE, FAKE, 0, None, FAKE, 0, 8, 8, 32, FAKE, 8, None) == 1
+    assert g(FAKE, FAKE, 0, FAKE, FAKE, 0, 8, 8, 32, None, 8, None) == 1
+    assert g(FAKE + 4, FAKE, 0, FAKE, FAKE, 0, 8, 8, 32, FAKE, 8, None) == 3
+    assert g(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 8, 32, FAKE, 8, None) == 0
+
+
+def test_python_binding_raises_without_gpu_tensors():
+    import torch
+    from adaptive_block_scaled_amd import if4
+    with pytest.raises(ValueError):
+        if4.quantize(torch.zeros(4, 32))
