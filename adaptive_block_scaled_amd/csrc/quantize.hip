@@ -104,11 +104,13 @@ __device__ __forceinline__ void load_group(const void* __restrict__ x, int64_t o
     }
 }
 
+// ---------------------------------------------------------------------------
+// Exact reference path (any fp32 input): thresholds compared exactly.
 template <bool kBf16, int kMode>
 __global__ void __launch_bounds__(kThreads)
-quantize_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
-                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
-                float p_negexp) {
+quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
+                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
+                      float p_negexp) {
     const int64_t ngroups = rows * gpr;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < ngroups; g += stride) {
@@ -163,6 +165,167 @@ quantize_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t l
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fast bf16 path.  Same results as the exact path for every bf16 input (the
+// GPU tests sweep every (bf16 x, E4M3 s') pair), with cheaper arithmetic:
+//
+//  * scale: RNE_E4M3(a/6) from fl(a * fl(1/6)).  fl(1/6) is 1/6 (1 - e) with
+//    e < 2^-25, so a tie a/6 = M (an E4M3 midpoint, 5 bits) rounds back to M
+//    exactly, and a bf16 a (8 bits) is never within 2^-9 relative of any other
+//    midpoint, far beyond the product's error.
+//  * codes: u = |x|/s is approximated as |x| * RN(1/s) and snapped to a 2^-18
+//    grid in the same fma (adding 48 puts the sum in [32, 64), whose fp32
+//    spacing is 2^-18).  Every midpoint of either grid is a multiple of 2^-18
+//    and the approximation error is below 2^-20, so a value exactly on a
+//    midpoint snaps onto it and every other value stays on its side (a bf16
+//    x sits at least 2^-16 from any midpoint of u or 7u/6 that it does not
+//    hit).  FP4: the snapped value carries x's sign into the hardware E2M1
+//    conversion (round to nearest even, saturating, signed zero kept), and
+//    the same hardware decodes the codes back for the error.  INT4: adding
+//    1.5 * 2^23 - 48 rounds the snapped 7|x|/(6s) to an integer (ties even),
+//    min() clamps it to 7, and the low bits of the float are |q|.
+//  * errors: for bf16 x every d = 7x - c*7s or 7|x| - |q|*6s is exact in
+//    fp32, so fma(-c, 7s, 7x) equals the reference fma(|x|, 7, -|c|*7s).
+//  * non-finite: a NaN reaches the FP4 error sum (NaN) and an infinity the
+//    absmax; zero-scale groups use a zero reciprocal so their sums stay finite.
+template <int kMode, bool kContig>
+__global__ void __launch_bounds__(kThreads)
+quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
+                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
+                     float p_negexp) {
+    __shared__ float2 recip[128];  // (RN(1/s'), RN(7/(6 s'))) per scale code; 0 for code 0
+    if (threadIdx.x < 128) {
+        const uint32_t c = threadIdx.x;
+        float2 t = make_float2(0.0f, 0.0f);
+        if (c != 0 && c != 127) {
+            const float sp = e4m3_value(c);
+            t = make_float2(1.0f / sp, 7.0f / (6.0f * sp));
+        }
+        recip[c] = t;
+    }
+    __syncthreads();
+
+    const int64_t ngroups = rows * gpr;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < ngroups; g += stride) {
+        int64_t off;
+        if constexpr (kContig) {
+            off = g * 16;
+        } else {
+            const int64_t r = g / gpr;
+            off = r * ld_x + (g - r * gpr) * 16;
+        }
+        const uint4* p = reinterpret_cast<const uint4*>(x + off);
+        const uint4 va = p[0], vb = p[1];
+        const uint32_t w[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+
+        // scale code: RNE_E4M3(a * 2^-E / 6), saturating at 448
+        const float q6 = (a * p_negexp) * 0.16666667f;
+        uint32_t sc;
+        if (q6 < 0.015625f) {
+            sc = (uint32_t)__builtin_rintf(q6 * 512.0f);
+        } else {
+            uint32_t b = __float_as_uint(q6);
+            b = b + 0x7FFFFu + ((b >> 20) & 1u);
+            sc = (b >> 20) - 960u;
+            sc = sc < 0x7Eu ? sc : 0x7Eu;
+        }
+        const float s = e4m3_value(sc) * p_exp;
+        const float2 rc = recip[sc];
+        const float inv_s = rc.x * p_negexp, k7 = rc.y * p_negexp;
+        const float s7 = 7.0f * s, s6 = 6.0f * s;
+
+        // FP4 codes via the hardware E2M1 conversion of the snapped quotients
+        float us[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float t = __builtin_fmaf(__builtin_fabsf(v[i]), inv_s, 48.0f) - 48.0f;
+            us[i] = __builtin_copysignf(t, v[i]);
+        }
+        uint32_t f0 = 0, f1 = 0;
+        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[0], us[1], 1.0f, 0);
+        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[2], us[3], 1.0f, 1);
+        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[4], us[5], 1.0f, 2);
+        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[6], us[7], 1.0f, 3);
+        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[8], us[9], 1.0f, 0);
+        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[10], us[11], 1.0f, 1);
+        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[12], us[13], 1.0f, 2);
+        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[14], us[15], 1.0f, 3);
+        float c[16];
+        {
+            auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 0);
+            auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 1);
+            auto d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 2);
+            auto d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 3);
+            auto d4 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 0);
+            auto d5 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 1);
+            auto d6 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 2);
+            auto d7 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 3);
+            c[0] = d0[0]; c[1] = d0[1]; c[2] = d1[0]; c[3] = d1[1];
+            c[4] = d2[0]; c[5] = d2[1]; c[6] = d3[0]; c[7] = d3[1];
+            c[8] = d4[0]; c[9] = d4[1]; c[10] = d5[0]; c[11] = d5[1];
+            c[12] = d6[0]; c[13] = d6[1]; c[14] = d7[0]; c[15] = d7[1];
+        }
+
+        // INT4 magnitudes and both error sums, index order 0..15
+        float ef = 0.0f, ei = 0.0f;
+        uint32_t rq[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float xa = __builtin_fabsf(v[i]);
+            const float X = 7.0f * v[i];
+            const float t = __builtin_fmaf(xa, k7, 48.0f);
+            const float r = __builtin_fminf(t + 12582864.0f, 12582919.0f);  // 1.5*2^23 + |q|
+            rq[i] = __float_as_uint(r);
+            const float q = r - 12582912.0f;
+            const float df = __builtin_fmaf(-c[i], s7, X);
+            const float di = __builtin_fmaf(-q, s6, __builtin_fabsf(X));
+            ef = __builtin_fmaf(df, df, ef);
+            ei = __builtin_fmaf(di, di, ei);
+        }
+        // gather |q| (low byte of each float) into nibbles: even elements in
+        // bits 0-2, odd elements in bits 4-6 of each byte
+        uint32_t i0, i1;
+        {
+            const uint32_t e0 = __builtin_amdgcn_perm(rq[2], rq[0], 0x0C0C0400u) |
+                                __builtin_amdgcn_perm(rq[6], rq[4], 0x04000C0Cu);
+            const uint32_t o0 = __builtin_amdgcn_perm(rq[3], rq[1], 0x0C0C0400u) |
+                                __builtin_amdgcn_perm(rq[7], rq[5], 0x04000C0Cu);
+            const uint32_t e1 = __builtin_amdgcn_perm(rq[10], rq[8], 0x0C0C0400u) |
+                                __builtin_amdgcn_perm(rq[14], rq[12], 0x04000C0Cu);
+            const uint32_t o1 = __builtin_amdgcn_perm(rq[11], rq[9], 0x0C0C0400u) |
+                                __builtin_amdgcn_perm(rq[15], rq[13], 0x04000C0Cu);
+            // sign bits are those of the FP4 codes (both take x's sign bit)
+            i0 = (e0 | (o0 << 4)) | (f0 & 0x88888888u);
+            i1 = (e1 | (o1 << 4)) | (f1 & 0x88888888u);
+        }
+
+        const bool use_int4 = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
+        uint32_t lo = use_int4 ? i0 : f0;
+        uint32_t hi = use_int4 ? i1 : f1;
+        uint32_t byte = sc | (use_int4 ? 0x80u : 0u);
+        if (sc == 0) {
+            lo = hi = 0;
+            byte = 0;
+        }
+        if (!(a <= 3.40282347e38f) || ef != ef) {  // infinity or NaN in the group
+            lo = hi = 0;
+            byte = 0x7Fu;
+        }
+        *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(lo, hi);
+        scales[g] = (uint8_t)byte;
+    }
+}
+
 template <bool kBf16, int kMode>
 hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                   uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
@@ -170,9 +333,19 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
     const int64_t ngroups = rows * gpr;
     int64_t blocks = (ngroups + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((quantize_kernel<kBf16, kMode>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, x, rows, gpr, ld_x, codes, scales, pow2f(scale_exp),
-                       pow2f(-scale_exp));
+    const float pe = pow2f(scale_exp), pn = pow2f(-scale_exp);
+    if constexpr (kBf16) {
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+        if (ld_x == cols)
+            hipLaunchKernelGGL((quantize_bf16_kernel<kMode, true>), dim3((unsigned)blocks),
+                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales, pe, pn);
+        else
+            hipLaunchKernelGGL((quantize_bf16_kernel<kMode, false>), dim3((unsigned)blocks),
+                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales, pe, pn);
+    } else {
+        hipLaunchKernelGGL((quantize_exact_kernel<false, kMode>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales, pe, pn);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the IF4 hot path on one MI355X.
+
+Step = one pass of the FFN-shaped IF4 pipeline on one batch of synthetic
+input, the largest single-GPU workload: quantize the weight W (bf16
+28672x8192, 0.02 * Student-t(4)) and the activation A (bf16 8192x8192,
+N(0,1) with 8 outlier columns x50) to IF4 along K = 8192, then the IF4 x IF4
+GEMM C[8192, 28672] = A W^T in fp32.  Inputs are resident in HBM before the
+timed region.  `value` is the step's throughput counted as the GEMM's
+2*M*N*K flops per step time (TFLOP/s); per-kernel figures (quantize GB/s
+against the 8 TB/s HBM peak, GEMM TFLOP/s against the 2.5 PFLOP/s dense
+fp16 MFMA peak, and the dequantize kernel timed after the step loop) are in
+`kernels`, and `roofline` reports the dominant kernel.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+METRIC = "IF4 quantize GB/s (% of HBM peak); IF4 W4A4 GEMM TFLOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def quant_bytes(rows, cols, in_bytes=2):
+    """Algorithmic bytes of one quantize: read the input, write 4-bit codes
+    and one scale byte per 16 values (2.5625 B per bf16 element)."""
+    n = rows * cols
+    return n * in_bytes + n // 2 + n // 16
+
+
+def dequant_bytes(rows, cols, out_bytes=2):
+    n = rows * cols
+    return n // 2 + n // 16 + n * out_bytes
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU oracle baseline (for profiler runs)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--cpu-budget-s", type=float, default=15.0,
+                   help="approximate CPU seconds for the oracle baseline sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the IF4 path here has no multi-GPU sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from adaptive_block_scaled_amd import if4, workloads as wl
+
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 28672, 8192
+
+    t0 = time.time()
+    a_t, w_t = wl.c5_ffn()
+    ea, ew = a_t.scale_exp, w_t.scale_exp
+    log(f"generated inputs in {time.time() - t0:.1f}s (E_A={ea}, E_W={ew})")
+    a_host, w_host = a_t.values, w_t.values
+    A = torch.from_numpy(a_host).to(torch.bfloat16).to(dev)
+    W = torch.from_numpy(w_host).to(torch.bfloat16).to(dev)
+    ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    wc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    Y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if4.quantize(W, ew, out=(wc, ws))
+        if ev is not None:
+            ev[1].record()
+        if4.quantize(A, ea, out=(ac, as_))
+        if ev is not None:
+            ev[2].record()
+        if4.gemm(ac, as_, ea, wc, ws, ew, out=C)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_qw = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    ms_qa = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_gemm = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    ms_step = wall * 1e3 / args.steps
+
+    # dequantize of A's codes to bf16, timed on its own after the step loop
+    ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(2):
+        if4.dequantize(ac, as_, ea, torch.bfloat16, out=Y)
+    ev_d[0].record()
+    nd = 10
+    for _ in range(nd):
+        if4.dequantize(ac, as_, ea, torch.bfloat16, out=Y)
+    ev_d[1].record()
+    torch.cuda.synchronize()
+    ms_deq = ev_d[0].elapsed_time(ev_d[1]) / nd
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
+    qw_b, qa_b = quant_bytes(N, K), quant_bytes(M, K)
+    qw_gbs = qw_b / (ms_qw * 1e-3) / 1e9
+    qa_gbs = qa_b / (ms_qa * 1e-3) / 1e9
+    deq_gbs = dequant_bytes(M, K) / (ms_deq * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    kernels = {
+        "quantize_W": {"ms": round(ms_qw, 4), "bytes": qw_b, "GB/s": round(qw_gbs, 1),
+                        "frac_hbm_peak": round(qw_gbs / HBM_PEAK_GBS, 4)},
+        "quantize_A": {"ms": round(ms_qa, 4), "bytes": qa_b, "GB/s": round(qa_gbs, 1),
+                        "frac_hbm_peak": round(qa_gbs / HBM_PEAK_GBS, 4)},
+        "gemm": {"ms": round(ms_gemm, 4), "flop": flops, "TFLOP/s": round(gemm_tflops, 1),
+                 "frac_mfma_peak": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
+        "dequantize_A_bf16": {"ms": round(ms_deq, 4), "bytes": dequant_bytes(M, K),
+                              "GB/s": round(deq_gbs, 1),
+                              "frac_hbm_peak": round(deq_gbs / HBM_PEAK_GBS, 4)},
+    }
+    roofline = {"kernel": "gemm", "bound": "mfma", "achieved": round(gemm_tflops, 1),
+                "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(a_host, w_host, ea, ew, M, N, K, args.cpu_budget_s)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ffn_if4_pipeline: quantize W bf16 28672x8192 (0.02*t4) + quantize A "
+                        "bf16 8192x8192 (N(0,1), 8 outlier cols x50) + IF4 W4A4 GEMM "
+                        "M=8192 N=28672 K=8192, fp32 out",
+            "M": M, "N": N, "K": K, "group": 16, "scale_exp_A": ea, "scale_exp_W": ew,
+            "parallelism": "single-gpu",
+        },
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(a_host, w_host, ea, ew, M, N, K, budget_s):
+    """The CPU oracle timed on a bounded sample of the same step: quantize a
+    row sample of W and A, then the fp64 GEMM oracle on a sample of output
+    rows (all N columns); each part is scaled to full size."""
+    import oracle
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    oracle.lib()
+    rw, ra = 1024, 512
+    t = time.perf_counter()
+    wc, ws = oracle.quantize(w_host[:rw], ew, nthreads=nthreads)
+    t_qw = (time.perf_counter() - t) * (N / rw)
+    t = time.perf_counter()
+    ac, as_ = oracle.quantize(a_host[:ra], ea, nthreads=nthreads)
+    t_qa = (time.perf_counter() - t) * (M / ra)
+    # GEMM: probe one output row on 1024 columns, then size the row sample
+    cols = np.arange(rw, dtype=np.int64)
+    t = time.perf_counter()
+    oracle.gemm_sample_f64(ac, as_, ea, wc, ws, ew, rows=[0], cols=cols, nthreads=nthreads)
+    per_row_cols = time.perf_counter() - t
+    n_rows = int(max(1, min(ra, budget_s / max(per_row_cols, 1e-6))))
+    t = time.perf_counter()
+    oracle.gemm_sample_f64(ac, as_, ea, wc, ws, ew, rows=np.arange(n_rows), cols=cols,
+                           nthreads=nthreads)
+    t_g = (time.perf_counter() - t) * (M / n_rows) * (N / rw)
+    total = t_qw + t_qa + t_g
+    return {
+        "value": round(2.0 * M * N * K / total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": (f"oracle quantize of {rw} W rows and {ra} A rows, fp64 GEMM oracle on "
+                   f"{n_rows} rows x {rw} cols; each part scaled to full size "
+                   f"(quantize W {t_qw:.1f}s, A {t_qa:.1f}s, GEMM {t_g:.0f}s per step)"),
+    }
+
+
+if __name__ == "__main__":
+    main()
