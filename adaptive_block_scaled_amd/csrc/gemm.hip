@@ -12,24 +12,24 @@
 // 2^(E_A + E_W) is applied in the epilogue, so every decoded value stays in
 // fp16's normal range (2^-10 .. 2688).
 //
-// Tiling: 256x256 output tile per workgroup of 8 waves (2 x 4), each wave
-// 128x64 (4 x 2 MFMA blocks of 32x32, 128 fp32 accumulators per lane).
-// K advances in slabs of 64 (four groups): every thread loads one row's
-// 32 code bytes and 4 scale bytes of the next slab while the waves run the
-// current slab's MFMAs from the other LDS buffer, then decodes and stores
-// them; one barrier per slab.  LDS: 2 buffers x 512 rows x 144 B (128 B of
-// fp16 + 16 B pad, which spreads the ds_read_b128/ds_write_b128 of
-// consecutive rows over all banks) + a 1 KB table of group scales.
+// Tiling: 256x256 output tile per workgroup of 4 waves (2 x 2), each wave
+// 128x128 (4 x 4 MFMA blocks of 32x32, 256 fp32 accumulators per lane in
+// AGPRs, one wave per SIMD).
+// K advances in slabs of 64 (four groups).  While the waves run the 64
+// MFMAs of slab s from one LDS buffer, every thread decodes its A row and
+// W row of slab s+1 into the other buffer, one group per 16-deep MFMA step,
+// and right after decoding a group reloads that group's registers with the
+// same group of slab s+2 -- so each load has a whole slab of MFMA work to
+// arrive in, with one register set and no copies.  One barrier per slab.
+// LDS: 2 buffers x 512 rows x 144 B (128 B of fp16 + 16 B pad, which spreads
+// the ds_read_b128/ds_write_b128 of consecutive rows over all banks).
+// Rows past M or N and groups past K load an in-range neighbour and decode
+// with a zero scale, so there are no branches around the loads.
 //
-// Decode of one group (branch-free; the flag only picks two table words and
-// the scale): the nibble magnitudes index an 8-entry byte table with
-// v_perm_b32 -- the table holds the fp16 high byte of each FP4 value
-// (0, .5, 1, 1.5, 2, 3, 4, 6) or INT4 magnitude (0..7); all of them have a
-// zero low byte -- the sign bit is moved to bit 15, and a packed fp16
-// multiply applies the group scale.  Nibbles j and j+4 of a code word form
-// one fp16 pair, so a group lands in LDS in the order
-// 0,4,1,5,2,6,3,7 | 8,12,9,13,10,14,11,15; A and W use the same order, so
-// the dot products are unchanged.
+// Decode of one group is branch-free (the flag only picks a shift, a mask
+// and a power-of-two conversion scale): see decode_word.  A group lands in
+// LDS in the order 0,2,4,6,1,3,5,7 | 8,10,12,14,9,11,13,15; A and W use the
+// same order, so the dot products are unchanged.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,26 +43,14 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WAVES_M = 2, WAVES_N = 4;
-constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // 128 x 64 per wave
-constexpr int FM = TM / 32, FN = TN / 32;            // 4 x 2 MFMA blocks
-constexpr int kThreads = 64 * WAVES_M * WAVES_N;     // 512
+constexpr int WAVES_M = 2, WAVES_N = 2;
+constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // 128 x 128 per wave
+constexpr int FM = TM / 32, FN = TN / 32;            // 4 x 4 MFMA blocks
+constexpr int kThreads = 64 * WAVES_M * WAVES_N;     // 256
 constexpr int ROW_BYTES = BK * 2 + 16;               // 144
 constexpr int BUF_BYTES = (BM + BN) * ROW_BYTES;     // 73728
-constexpr int SIGMA_OFF = 2 * BUF_BYTES;
-constexpr int SMEM_BYTES = SIGMA_OFF + 256 * 4;      // 148480
-static_assert(BM + BN == kThreads, "one thread per tile row");
-
-// fp16 high bytes of the 8 magnitudes, packed as v_perm_b32 table words
-// (bytes 0-3 from the low word, 4-7 from the high word).
-constexpr uint32_t FP4_LO = 0x3E3C3800u;  // 0, .5, 1, 1.5
-constexpr uint32_t FP4_HI = 0x46444240u;  // 2, 3, 4, 6
-constexpr uint32_t INT_LO = 0x42403C00u;  // 0, 1, 2, 3
-constexpr uint32_t INT_HI = 0x47464544u;  // 4, 5, 6, 7
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
+constexpr int SMEM_BYTES = 2 * BUF_BYTES;            // 147456
+static_assert(BM == kThreads && BN == kThreads, "one A row and one W row per thread");
 
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     half2v x = __builtin_bit_cast(half2v, a);
@@ -70,107 +58,140 @@ __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, x * y);
 }
 
-// Decode one code word (8 nibbles) of a group into 4 fp16 pairs.
-__device__ __forceinline__ void decode_word(uint32_t w, uint32_t tlo, uint32_t thi,
-                                            uint32_t sig2, uint32_t (&out)[4]) {
-    const uint32_t w4 = w << 4, w8 = w << 8, w12 = w << 12, wr4 = w >> 4;
-    const uint32_t m_sel = 0x07000700u, z_sel = 0x000C000Cu, sgn = 0x80008000u;
-    // pair j = (nibble j, nibble j + 4): magnitudes to bytes 1 and 3 of the
-    // selector (bytes 0 and 2 select zero), signs to bits 15 and 31
-    out[0] = pk_mul(perm(thi, tlo, (w8 & m_sel) | z_sel) | (w12 & sgn), sig2);
-    out[1] = pk_mul(perm(thi, tlo, (w4 & m_sel) | z_sel) | (w8 & sgn), sig2);
-    out[2] = pk_mul(perm(thi, tlo, (w & m_sel) | z_sel) | (w4 & sgn), sig2);
-    out[3] = pk_mul(perm(thi, tlo, (wr4 & m_sel) | z_sel) | (w & sgn), sig2);
-}
-
-__device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, uint32_t b,
-                                             const uint32_t* __restrict__ sigma,
-                                             uint32_t (&h)[8]) {
-    const bool int4 = (b & 0x80u) != 0;
-    const uint32_t tlo = int4 ? INT_LO : FP4_LO;
-    const uint32_t thi = int4 ? INT_HI : FP4_HI;
-    const uint32_t sig2 = sigma[b];
-    uint32_t a[4], c[4];
-    decode_word(w0, tlo, thi, sig2, a);
-    decode_word(w1, tlo, thi, sig2, c);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        h[i] = a[i];
-        h[4 + i] = c[i];
-    }
-}
-
-struct Packed {
-    uint4 c0, c1;  // 32 code bytes = 4 groups of one row
-    uint32_t b;    // 4 scale bytes
+// One group's packed data in registers: 16 nibbles and the scale byte.  The
+// loaded values are only consumed by the decode one slab later, so nothing
+// may touch them right after the load (that would force a wait).
+struct Group {
+    uint32_t w0, w1;
+    uint32_t b;
 };
 
-// Codes are only guaranteed 8-byte aligned (rows are K/2 bytes, K a
-// multiple of 16), so the 32 bytes of a row's slab are read as four 8-byte
-// loads.
-__device__ __forceinline__ void load_slab(const uint8_t* __restrict__ codes,
-                                          const uint8_t* __restrict__ scales, int64_t row,
-                                          int64_t rows, int64_t K, int64_t gpr, int64_t k0,
-                                          Packed& p) {
-    uint2 q0 = make_uint2(0u, 0u), q1 = q0, q2 = q0, q3 = q0;
-    uint32_t b = 0;
-    if (row < rows) {
-        const int64_t g0 = k0 / 16;
-        const int64_t ng = gpr - g0;  // >= 1
-        const uint2* cp = reinterpret_cast<const uint2*>(codes + row * (K / 2) + k0 / 2);
-        const uint8_t* sp = scales + row * gpr + g0;
-        q0 = cp[0];
-        b = sp[0];
-        if (ng > 1) {
-            q1 = cp[1];
-            b |= (uint32_t)sp[1] << 8;
-        }
-        if (ng > 2) {
-            q2 = cp[2];
-            b |= (uint32_t)sp[2] << 16;
-        }
-        if (ng > 3) {  // a K tail leaves fewer than 4 groups; the rest decode to 0
-            q3 = cp[3];
-            b |= (uint32_t)sp[3] << 24;
-        }
-    }
-    p.c0 = make_uint4(q0.x, q0.y, q1.x, q1.y);
-    p.c1 = make_uint4(q2.x, q2.y, q3.x, q3.y);
-    p.b = b;
+// Decode one code word (8 nibbles) into 4 fp16 pairs.  Each nibble becomes
+// an E4M3 byte: FP4 s.e1e0.m -> s.00e1e0.m00, whose value is c * 2^-6; INT4
+// s.mmm -> s.0000.mmm, an E4M3 subnormal worth |q| * 2^-9.  The hardware
+// E4M3 -> fp16 conversion scales by 2^6 or 2^9 (exact), giving c or |q|, and
+// a packed fp16 multiply applies the group scale.  The even nibbles' bytes
+// and the odd nibbles' bytes are built in two words, so the pairs come out
+// as (0,2) (4,6) (1,3) (5,7).
+__device__ __forceinline__ void decode_word(uint32_t w, uint32_t sh, uint32_t rsh, uint32_t mask,
+                                            float cvt_scale, uint32_t sig2, uint32_t* out) {
+    const uint32_t ev = ((w << 4) & 0x80808080u) | ((w << sh) & mask);
+    const uint32_t od = (w & 0x80808080u) | ((w >> rsh) & mask);
+    out[0] = pk_mul(__builtin_bit_cast(uint32_t,
+                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, cvt_scale, false)), sig2);
+    out[1] = pk_mul(__builtin_bit_cast(uint32_t,
+                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, cvt_scale, true)), sig2);
+    out[2] = pk_mul(__builtin_bit_cast(uint32_t,
+                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, cvt_scale, false)), sig2);
+    out[3] = pk_mul(__builtin_bit_cast(uint32_t,
+                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, cvt_scale, true)), sig2);
 }
 
-__device__ __forceinline__ void store_slab(uint8_t* __restrict__ rowp, const Packed& p,
-                                           const uint32_t* __restrict__ sigma) {
-    const uint32_t w[8] = {p.c0.x, p.c0.y, p.c0.z, p.c0.w, p.c1.x, p.c1.y, p.c1.z, p.c1.w};
+// Decode a group to 16 fp16 values and store them (32 bytes) at dst.  The
+// group scale: s' from the E4M3 code by the hardware conversion (exact,
+// NaN for 0x7F), times fl32(6/7) for INT4, rounded once to fp16.
+__device__ __forceinline__ void decode_store(uint8_t* __restrict__ dst, const Group& g,
+                                             bool zero) {
+    const uint32_t b = g.b;
+    const float sp = __builtin_amdgcn_cvt_scalef32_f32_fp8(b & 0x7Fu, 1.0f, 0);
+    const bool int4 = (b & 0x80u) != 0;
+    float sig = int4 ? sp * 0.857142866f : sp;
+    sig = zero ? 0.0f : sig;
+    const uint32_t h16 = __builtin_bit_cast(uint16_t, (_Float16)sig);
+    const uint32_t sig2 = h16 | (h16 << 16);
+    const uint32_t sh = int4 ? 0u : 2u;
+    const uint32_t mask = 0x07070707u << sh;
+    const float cvt_scale = int4 ? 512.0f : 64.0f;
+    uint32_t h[8];
+    decode_word(g.w0, sh, 4u - sh, mask, cvt_scale, sig2, h);
+    decode_word(g.w1, sh, 4u - sh, mask, cvt_scale, sig2, h + 4);
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    d4[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    d4[1] = make_uint4(h[4], h[5], h[6], h[7]);
+}
+
+// Load group index gi (clamped into the row) of a row whose code and scale
+// rows start at cp and sp.  A group past K (or a row past M/N) decodes with
+// a zero scale, decided at decode time from the indices.
+__device__ __forceinline__ void load_group(const uint8_t* __restrict__ cp,
+                                           const uint8_t* __restrict__ sp, int64_t gi,
+                                           int64_t gpr, Group& g) {
+    const int64_t gc = gi < gpr ? gi : gpr - 1;
+    const uint2 q = *reinterpret_cast<const uint2*>(cp + gc * 8);
+    g.w0 = q.x;
+    g.w1 = q.y;
+    g.b = sp[gc];
+}
+
+// Slab register state of one row (A or W).  kWide: the slab's 32 code bytes
+// as two 16-byte words (groups 0-1, 2-3) and the 4 scale bytes as one word,
+// which needs 16-byte aligned code rows and K a multiple of 64; otherwise
+// one 8-byte word and one byte per group, clamped into the row.
+template <bool kWide>
+struct RowSlab;
+
+template <>
+struct RowSlab<true> {
+    uint4 c01, c23;
+    uint32_t sw;
+    uint32_t b[4];  // scale bytes of the slab being decoded
+    __device__ __forceinline__ void start_decode() {
+        // take the scale bytes out first, so the scale word can be reloaded
+        // at once (it then has a whole slab to arrive)
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        uint32_t h[8];
-        decode_group(w[2 * g], w[2 * g + 1], (p.b >> (8 * g)) & 0xFFu, sigma, h);
-        uint4* dst = reinterpret_cast<uint4*>(rowp + g * 32);
-        dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
-        dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        for (int g = 0; g < 4; g++) b[g] = (sw >> (8 * g)) & 0xFFu;
     }
-}
+    __device__ __forceinline__ Group group(int g) const {
+        const uint4 c = g < 2 ? c01 : c23;
+        Group r;
+        r.w0 = (g & 1) ? c.z : c.x;
+        r.w1 = (g & 1) ? c.w : c.y;
+        r.b = b[g];
+        return r;
+    }
+    // reload after group g of the current slab was decoded
+    __device__ __forceinline__ void refill(const uint8_t* __restrict__ cp,
+                                           const uint8_t* __restrict__ sp, int64_t slab, int g,
+                                           int64_t gpr) {
+        (void)gpr;
+        if (g == 0) sw = *reinterpret_cast<const uint32_t*>(sp + slab * 4);
+        if (g == 1) c01 = reinterpret_cast<const uint4*>(cp + slab * 32)[0];
+        if (g == 3) c23 = reinterpret_cast<const uint4*>(cp + slab * 32)[1];
+    }
+    __device__ __forceinline__ void load_all(const uint8_t* __restrict__ cp,
+                                             const uint8_t* __restrict__ sp, int64_t slab,
+                                             int64_t gpr) {
+        refill(cp, sp, slab, 0, gpr);
+        refill(cp, sp, slab, 1, gpr);
+        refill(cp, sp, slab, 3, gpr);
+    }
+};
 
-__device__ __forceinline__ uint32_t sigma_entry(uint32_t b) {
-    // fp16 group scale for scale byte b: s' for FP4, fl16(fl32(6 s'/7)) for
-    // INT4; NaN for the 0x7F/0xFF pattern.  Duplicated into both halves.
-    const uint32_t code = b & 0x7Fu;
-    float sp = code >= 8u ? __uint_as_float((code + 960u) << 20) : (float)code * 0.001953125f;
-    if (code == 0x7Fu) sp = __uint_as_float(0x7FC00000u);
-    const float v = (b & 0x80u) ? (6.0f * sp) / 7.0f : sp;
-    const _Float16 hv = (_Float16)v;
-    const uint32_t u = __builtin_bit_cast(uint16_t, hv);
-    return u | (u << 16);
-}
+template <>
+struct RowSlab<false> {
+    Group gr[4];
+    __device__ __forceinline__ void start_decode() {}
+    __device__ __forceinline__ Group group(int g) const { return gr[g]; }
+    __device__ __forceinline__ void refill(const uint8_t* __restrict__ cp,
+                                           const uint8_t* __restrict__ sp, int64_t slab, int g,
+                                           int64_t gpr) {
+        load_group(cp, sp, slab * 4 + g, gpr, gr[g]);
+    }
+    __device__ __forceinline__ void load_all(const uint8_t* __restrict__ cp,
+                                             const uint8_t* __restrict__ sp, int64_t slab,
+                                             int64_t gpr) {
+#pragma unroll
+        for (int g = 0; g < 4; g++) refill(cp, sp, slab, g, gpr);
+    }
+};
 
+template <bool kWide>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
             const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
             int64_t M, int64_t N, int64_t K, float* __restrict__ c, int64_t ldc, float out_scale,
             int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint32_t* sigma = reinterpret_cast<uint32_t*>(smem + SIGMA_OFF);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -187,16 +208,16 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t gpr = K / 16;
 
-    if (tid < 256) sigma[tid] = sigma_entry(tid);
-
-    // this thread's load/decode row: A rows 0..255, then W rows 0..255
-    const bool is_w = tid >= BM;
-    const int lr = is_w ? tid - BM : tid;
-    const uint8_t* codes = is_w ? w_codes : a_codes;
-    const uint8_t* scales = is_w ? w_scales : a_scales;
-    const int64_t grow = (is_w ? n0 : m0) + lr;
-    const int64_t grows = is_w ? N : M;
-    const int lds_row = tid;  // rows 0..255 = A tile, 256..511 = W tile
+    // this thread's A row and W row (clamped in range; dead rows decode to 0)
+    const int64_t arow = m0 + tid, wrow = n0 + tid;
+    const bool a_dead = arow >= M, w_dead = wrow >= N;
+    const int64_t ar = a_dead ? M - 1 : arow, wr = w_dead ? N - 1 : wrow;
+    const uint8_t* const acp = a_codes + ar * (K / 2);
+    const uint8_t* const asp = a_scales + ar * gpr;
+    const uint8_t* const wcp = w_codes + wr * (K / 2);
+    const uint8_t* const wsp = w_scales + wr * gpr;
+    uint8_t* const a_lds = smem + tid * ROW_BYTES;
+    uint8_t* const w_lds = smem + (BM + tid) * ROW_BYTES;
 
     float16v acc[FM][FN];
 #pragma unroll
@@ -207,40 +228,78 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     const int nslabs = (int)((K + BK - 1) / BK);
-    Packed p;
-    load_slab(codes, scales, grow, grows, K, gpr, 0, p);
-    __syncthreads();  // sigma table ready
-    store_slab(smem + lds_row * ROW_BYTES, p, sigma);
+    const int64_t last = nslabs - 1;
+    RowSlab<kWide> ra, rw;
+    ra.load_all(acp, asp, 0, gpr);
+    rw.load_all(wcp, wsp, 0, gpr);
+    ra.start_decode();
+    rw.start_decode();
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        decode_store(a_lds + g * 32, ra.group(g), a_dead || g >= gpr);
+        decode_store(w_lds + g * 32, rw.group(g), w_dead || g >= gpr);
+    }
+    ra.load_all(acp, asp, last < 1 ? last : 1, gpr);
+    rw.load_all(wcp, wsp, last < 1 ? last : 1, gpr);
     __syncthreads();
 
-    const int a_row0 = wm * TM + (lane & 31);
-    const int w_row0 = BM + wn * TN + (lane & 31);
-    const int koff = (lane >> 5) * 16;  // bytes: 8 halfs per lane half
+    const int a_off = (wm * TM + (lane & 31)) * ROW_BYTES + (lane >> 5) * 16;
+    const int w_off = (BM + wn * TN + (lane & 31)) * ROW_BYTES + (lane >> 5) * 16;
 
     for (int s = 0; s < nslabs; s++) {
         const uint8_t* buf = smem + (s & 1) * BUF_BYTES;
-        const bool more = s + 1 < nslabs;
-        if (more) load_slab(codes, scales, grow, grows, K, gpr, (int64_t)(s + 1) * BK, p);
+        uint8_t* nbuf = smem + ((s + 1) & 1) * BUF_BYTES;
+        // registers hold slab s+1 (decoded now) and are refilled with slab
+        // s+2, clamped: past the end the loads repeat the last slab and the
+        // decodes write a buffer nobody reads again
+        const int64_t sl = (int64_t)s + 2 < last ? (int64_t)s + 2 : last;
+        const int64_t gdec = (int64_t)(s + 1) * 4;  // first group decoded now
+        ra.start_decode();
+        rw.start_decode();
+        half8 av[2][FM], bv[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            av[0][i] = *reinterpret_cast<const half8*>(buf + a_off + i * 32 * ROW_BYTES);
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * 32 * ROW_BYTES);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
-            half8 av[FM], bv[FN];
+            const int cur = kk & 1;
+            if (kk + 1 < BK / 16) {
 #pragma unroll
-            for (int i = 0; i < FM; i++)
-                av[i] = *reinterpret_cast<const half8*>(buf + (a_row0 + 32 * i) * ROW_BYTES +
-                                                        kk * 32 + koff);
+                for (int i = 0; i < FM; i++)
+                    av[cur ^ 1][i] = *reinterpret_cast<const half8*>(
+                        buf + a_off + i * 32 * ROW_BYTES + (kk + 1) * 32);
 #pragma unroll
-            for (int j = 0; j < FN; j++)
-                bv[j] = *reinterpret_cast<const half8*>(buf + (w_row0 + 32 * j) * ROW_BYTES +
-                                                        kk * 32 + koff);
+                for (int j = 0; j < FN; j++)
+                    bv[cur ^ 1][j] = *reinterpret_cast<const half8*>(
+                        buf + w_off + j * 32 * ROW_BYTES + (kk + 1) * 32);
+            }
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j],
-                                                                       0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j],
+                                                                       acc[i][j], 0, 0, 0);
+            const bool past = gdec + kk >= gpr;  // group of slab s+1 beyond K
+            decode_store(nbuf + tid * ROW_BYTES + kk * 32, ra.group(kk), a_dead || past);
+            decode_store(nbuf + (BM + tid) * ROW_BYTES + kk * 32, rw.group(kk), w_dead || past);
+            ra.refill(acp, asp, sl, kk, gpr);
+            rw.refill(wcp, wsp, sl, kk, gpr);
+            // One wave per SIMD issues in order, so the decode only overlaps
+            // the MFMAs if it is interleaved with them: one MFMA (32 cycles
+            // in the matrix core), then a handful of VALU/LDS instructions.
+#pragma unroll
+            for (int i = 0; i < FM * FN; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more)
-            store_slab(smem + ((s + 1) & 1) * BUF_BYTES + lds_row * ROW_BYTES, p, sigma);
         __syncthreads();
     }
 
@@ -278,18 +337,29 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t 
         hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, c, M, N, ldc);
         return hipGetLastError();
     }
-    // LDS above 64 KB must be requested per kernel (idempotent, any device)
-    hipError_t err = hipFuncSetAttribute((const void*)gemm_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
-    if (err != hipSuccess) return err;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
     // 2^(a_exp + w_exp), exact; |a_exp + w_exp| <= 128 is split in two factors
     const int e = a_exp + w_exp;
     const float out_scale = pow2f(e / 2) * pow2f(e - e / 2);
-    hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads),
-                       SMEM_BYTES, stream, a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
-                       out_scale, (int)tiles_m, (int)tiles_n);
+    // Wide loads need 16-byte aligned code rows and 4-byte aligned scale rows
+    // with whole 64-deep slabs.
+    const bool wide = K % 64 == 0 && (uintptr_t)a_codes % 16 == 0 &&
+                      (uintptr_t)w_codes % 16 == 0 && (uintptr_t)a_scales % 4 == 0 &&
+                      (uintptr_t)w_scales % 4 == 0;
+    const void* fn = wide ? (const void*)gemm_kernel<true> : (const void*)gemm_kernel<false>;
+    // LDS above 64 KB must be requested per kernel (idempotent, any device)
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    if (err != hipSuccess) return err;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
+    if (wide)
+        hipLaunchKernelGGL(gemm_kernel<true>, grid, block, SMEM_BYTES, stream, a_codes, a_scales,
+                           w_codes, w_scales, M, N, K, c, ldc, out_scale, (int)tiles_m,
+                           (int)tiles_n);
+    else
+        hipLaunchKernelGGL(gemm_kernel<false>, grid, block, SMEM_BYTES, stream, a_codes, a_scales,
+                           w_codes, w_scales, M, N, K, c, ldc, out_scale, (int)tiles_m,
+                           (int)tiles_n);
     return hipGetLastError();
 }
 
