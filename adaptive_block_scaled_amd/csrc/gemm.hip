@@ -43,14 +43,30 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WAVES_M = 2, WAVES_N = 2;
-constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // 128 x 128 per wave
-constexpr int FM = TM / 32, FN = TN / 32;            // 4 x 4 MFMA blocks
-constexpr int kThreads = 64 * WAVES_M * WAVES_N;     // 256
-constexpr int ROW_BYTES = BK * 2 + 16;               // 144
-constexpr int BUF_BYTES = (BM + BN) * ROW_BYTES;     // 73728
-constexpr int SMEM_BYTES = 2 * BUF_BYTES;            // 147456
-static_assert(BM == kThreads && BN == kThreads, "one A row and one W row per thread");
+// LDS tiles are stored in MFMA-fragment order: for each block of 32 rows,
+// each 16-deep group and each half of it, the 32 rows' 16-byte pieces lie
+// next to each other, so a wave reads a whole 32x16 fragment as one
+// contiguous 1 KB ds_read_b128 and a decoding wave writes contiguous 512 B
+// runs.  Offset of (row R, group g, half h) inside an operand tile:
+constexpr int TILE_BYTES = 256 * BK * 2;             // 32 KB per operand
+constexpr int BUF_BYTES = 2 * TILE_BYTES;            // A tile, then W tile
+constexpr int SMEM_BYTES = 2 * BUF_BYTES;            // double-buffered: 128 KB
+__device__ __forceinline__ int frag_off(int R, int g, int h) {
+    return ((((R >> 5) * (BK / 16) + g) * 2 + h) * 32 + (R & 31)) * 16;
+}
+
+// Wave layout of a 256x256 tile: WM x WN waves, each (256/WM) x (256/WN).
+// With 4 waves every thread owns one A row and one W row; with 8 waves one
+// row of either.
+template <int WM, int WN>
+struct Layout {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr bool kTwoRows = kThreads == BM;
+    static_assert(kThreads == BM || kThreads == BM + BN, "one or two rows per thread");
+};
 
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     half2v x = __builtin_bit_cast(half2v, a);
@@ -90,8 +106,8 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t sh, uint32_t rs
 // Decode a group to 16 fp16 values and store them (32 bytes) at dst.  The
 // group scale: s' from the E4M3 code by the hardware conversion (exact,
 // NaN for 0x7F), times fl32(6/7) for INT4, rounded once to fp16.
-__device__ __forceinline__ void decode_store(uint8_t* __restrict__ dst, const Group& g,
-                                             bool zero) {
+__device__ __forceinline__ void decode_store(uint8_t* __restrict__ tile, int R, int gi,
+                                             const Group& g, bool zero) {
     const uint32_t b = g.b;
     const float sp = __builtin_amdgcn_cvt_scalef32_f32_fp8(b & 0x7Fu, 1.0f, 0);
     const bool int4 = (b & 0x80u) != 0;
@@ -105,9 +121,8 @@ __device__ __forceinline__ void decode_store(uint8_t* __restrict__ dst, const Gr
     uint32_t h[8];
     decode_word(g.w0, sh, 4u - sh, mask, cvt_scale, sig2, h);
     decode_word(g.w1, sh, 4u - sh, mask, cvt_scale, sig2, h + 4);
-    uint4* d4 = reinterpret_cast<uint4*>(dst);
-    d4[0] = make_uint4(h[0], h[1], h[2], h[3]);
-    d4[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    *reinterpret_cast<uint4*>(tile + frag_off(R, gi, 0)) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(tile + frag_off(R, gi, 1)) = make_uint4(h[4], h[5], h[6], h[7]);
 }
 
 // Load group index gi (clamped into the row) of a row whose code and scale
@@ -185,18 +200,21 @@ struct RowSlab<false> {
     }
 };
 
-template <bool kWide>
-__global__ void __launch_bounds__(kThreads)
+template <bool kWide, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
             const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
             int64_t M, int64_t N, int64_t K, float* __restrict__ c, int64_t ldc, float out_scale,
             int tiles_m, int tiles_n) {
+    using LY = Layout<WM, WN>;
+    constexpr int TM = LY::TM, TN = LY::TN, FM = LY::FM, FN = LY::FN;
+    constexpr bool kTwo = LY::kTwoRows;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wm = wave / WN, wn = wave % WN;
 
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
     // contiguous run of tiles, walking down M within a column of W tiles so
@@ -208,16 +226,24 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t gpr = K / 16;
 
-    // this thread's A row and W row (clamped in range; dead rows decode to 0)
-    const int64_t arow = m0 + tid, wrow = n0 + tid;
-    const bool a_dead = arow >= M, w_dead = wrow >= N;
-    const int64_t ar = a_dead ? M - 1 : arow, wr = w_dead ? N - 1 : wrow;
-    const uint8_t* const acp = a_codes + ar * (K / 2);
-    const uint8_t* const asp = a_scales + ar * gpr;
-    const uint8_t* const wcp = w_codes + wr * (K / 2);
-    const uint8_t* const wsp = w_scales + wr * gpr;
-    uint8_t* const a_lds = smem + tid * ROW_BYTES;
-    uint8_t* const w_lds = smem + (BM + tid) * ROW_BYTES;
+    // Rows this thread loads and decodes (clamped in range; dead rows decode
+    // to 0).  Row 0: A row tid (4 waves) or tile row tid of A-then-W (8
+    // waves); row 1 (4 waves only): W row tid.
+    const bool r0_is_w = !kTwo && tid >= BM;
+    const int lr0 = r0_is_w ? tid - BM : tid;
+    const int64_t g0row = (r0_is_w ? n0 : m0) + lr0;
+    const int64_t lim0 = r0_is_w ? N : M;
+    const bool dead0 = g0row >= lim0;
+    const int64_t cr0 = dead0 ? lim0 - 1 : g0row;
+    const uint8_t* const cp0 = (r0_is_w ? w_codes : a_codes) + cr0 * (K / 2);
+    const uint8_t* const sp0 = (r0_is_w ? w_scales : a_scales) + cr0 * gpr;
+    const int tile0 = r0_is_w ? TILE_BYTES : 0;  // operand tile of row 0
+    const int64_t wrow = n0 + tid;
+    const bool dead1 = wrow >= N;
+    const int64_t cr1 = dead1 ? N - 1 : wrow;
+    const uint8_t* const cp1 = w_codes + cr1 * (K / 2);
+    const uint8_t* const sp1 = w_scales + cr1 * gpr;
+    const int tile1 = TILE_BYTES;
 
     float16v acc[FM][FN];
 #pragma unroll
@@ -229,23 +255,32 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 
     const int nslabs = (int)((K + BK - 1) / BK);
     const int64_t last = nslabs - 1;
-    RowSlab<kWide> ra, rw;
-    ra.load_all(acp, asp, 0, gpr);
-    rw.load_all(wcp, wsp, 0, gpr);
-    ra.start_decode();
-    rw.start_decode();
+    RowSlab<kWide> r0, r1;
+    r0.load_all(cp0, sp0, 0, gpr);
+    if (kTwo) r1.load_all(cp1, sp1, 0, gpr);
+    r0.start_decode();
+    if (kTwo) r1.start_decode();
 #pragma unroll
     for (int g = 0; g < 4; g++) {
-        decode_store(a_lds + g * 32, ra.group(g), a_dead || g >= gpr);
-        decode_store(w_lds + g * 32, rw.group(g), w_dead || g >= gpr);
+        decode_store(smem + tile0, lr0, g, r0.group(g), dead0 || g >= gpr);
+        if (kTwo) decode_store(smem + tile1, tid, g, r1.group(g), dead1 || g >= gpr);
     }
-    ra.load_all(acp, asp, last < 1 ? last : 1, gpr);
-    rw.load_all(wcp, wsp, last < 1 ? last : 1, gpr);
+    r0.load_all(cp0, sp0, last < 1 ? last : 1, gpr);
+    if (kTwo) r1.load_all(cp1, sp1, last < 1 ? last : 1, gpr);
     __syncthreads();
 
-    const int a_off = (wm * TM + (lane & 31)) * ROW_BYTES + (lane >> 5) * 16;
-    const int w_off = (BM + wn * TN + (lane & 31)) * ROW_BYTES + (lane >> 5) * 16;
+    // fragment (block i, group kk) of this wave: frag_off(first row, kk, 0) + lane * 16
+    const int a_off = frag_off(wm * TM, 0, 0) + lane * 16;
+    const int w_off = TILE_BYTES + frag_off(wn * TN, 0, 0) + lane * 16;
+    constexpr int FRAG_BLOCK = (BK / 16) * 2 * 32 * 16;  // bytes between 32-row blocks
+    constexpr int FRAG_GROUP = 2 * 32 * 16;              // bytes between groups
 
+    // With two waves per SIMD (8 waves; waves w and w+4 share a SIMD) the
+    // pair runs in opposite phases inside every slab: one wave issues its
+    // MFMAs while its partner decodes, then they swap, so the matrix core
+    // and the VALU work at the same time.  With one wave per SIMD the decode
+    // is interleaved with the MFMAs instead.
+    const bool mfma_first = kTwo || wave < 4;
     for (int s = 0; s < nslabs; s++) {
         const uint8_t* buf = smem + (s & 1) * BUF_BYTES;
         uint8_t* nbuf = smem + ((s + 1) & 1) * BUF_BYTES;
@@ -254,15 +289,26 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         // decodes write a buffer nobody reads again
         const int64_t sl = (int64_t)s + 2 < last ? (int64_t)s + 2 : last;
         const int64_t gdec = (int64_t)(s + 1) * 4;  // first group decoded now
-        ra.start_decode();
-        rw.start_decode();
+        r0.start_decode();
+        if (kTwo) r1.start_decode();
+        auto decode_group = [&](int kk) {
+            const bool past = gdec + kk >= gpr;  // group of slab s+1 beyond K
+            decode_store(nbuf + tile0, lr0, kk, r0.group(kk), dead0 || past);
+            if (kTwo) decode_store(nbuf + tile1, tid, kk, r1.group(kk), dead1 || past);
+            r0.refill(cp0, sp0, sl, kk, gpr);
+            if (kTwo) r1.refill(cp1, sp1, sl, kk, gpr);
+        };
+        if (!mfma_first) {
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; kk++) decode_group(kk);
+        }
         half8 av[2][FM], bv[2][FN];
 #pragma unroll
         for (int i = 0; i < FM; i++)
-            av[0][i] = *reinterpret_cast<const half8*>(buf + a_off + i * 32 * ROW_BYTES);
+            av[0][i] = *reinterpret_cast<const half8*>(buf + a_off + i * FRAG_BLOCK);
 #pragma unroll
         for (int j = 0; j < FN; j++)
-            bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * 32 * ROW_BYTES);
+            bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
             const int cur = kk & 1;
@@ -270,11 +316,11 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 #pragma unroll
                 for (int i = 0; i < FM; i++)
                     av[cur ^ 1][i] = *reinterpret_cast<const half8*>(
-                        buf + a_off + i * 32 * ROW_BYTES + (kk + 1) * 32);
+                        buf + a_off + i * FRAG_BLOCK + (kk + 1) * FRAG_GROUP);
 #pragma unroll
                 for (int j = 0; j < FN; j++)
                     bv[cur ^ 1][j] = *reinterpret_cast<const half8*>(
-                        buf + w_off + j * 32 * ROW_BYTES + (kk + 1) * 32);
+                        buf + w_off + j * FRAG_BLOCK + (kk + 1) * FRAG_GROUP);
             }
 #pragma unroll
             for (int i = 0; i < FM; i++)
@@ -282,23 +328,24 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                 for (int j = 0; j < FN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j],
                                                                        acc[i][j], 0, 0, 0);
-            const bool past = gdec + kk >= gpr;  // group of slab s+1 beyond K
-            decode_store(nbuf + tid * ROW_BYTES + kk * 32, ra.group(kk), a_dead || past);
-            decode_store(nbuf + (BM + tid) * ROW_BYTES + kk * 32, rw.group(kk), w_dead || past);
-            ra.refill(acp, asp, sl, kk, gpr);
-            rw.refill(wcp, wsp, sl, kk, gpr);
-            // One wave per SIMD issues in order, so the decode only overlaps
-            // the MFMAs if it is interleaved with them: one MFMA (32 cycles
-            // in the matrix core), then a handful of VALU/LDS instructions.
+            if (kTwo) {
+                decode_group(kk);
+                // One MFMA (32 cycles in the matrix core), then a handful of
+                // VALU/LDS/global instructions.
 #pragma unroll
-            for (int i = 0; i < FM * FN; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+                for (int i = 0; i < FM * FN; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!kTwo && mfma_first) {
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; kk++) decode_group(kk);
         }
         __syncthreads();
     }
@@ -326,6 +373,28 @@ __global__ void zero_kernel(float* __restrict__ c, int64_t M, int64_t N, int64_t
         c[(i / N) * ldc + (i % N)] = 0.0f;
 }
 
+
+#ifndef IF4_GEMM_WM
+#define IF4_GEMM_WM 4
+#define IF4_GEMM_WN 2
+#endif
+
+template <bool kWide>
+hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                       const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* c,
+                       int64_t ldc, float out_scale, int64_t tiles_m, int64_t tiles_n,
+                       hipStream_t stream) {
+    constexpr int WM = IF4_GEMM_WM, WN = IF4_GEMM_WN;
+    const void* fn = (const void*)gemm_kernel<kWide, WM, WN>;
+    // LDS above 64 KB must be requested per kernel (idempotent, any device)
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gemm_kernel<kWide, WM, WN>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(Layout<WM, WN>::kThreads), SMEM_BYTES, stream, a_codes, a_scales,
+                       w_codes, w_scales, M, N, K, c, ldc, out_scale, (int)tiles_m, (int)tiles_n);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t a_exp,
@@ -347,20 +416,10 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t 
     const bool wide = K % 64 == 0 && (uintptr_t)a_codes % 16 == 0 &&
                       (uintptr_t)w_codes % 16 == 0 && (uintptr_t)a_scales % 4 == 0 &&
                       (uintptr_t)w_scales % 4 == 0;
-    const void* fn = wide ? (const void*)gemm_kernel<true> : (const void*)gemm_kernel<false>;
-    // LDS above 64 KB must be requested per kernel (idempotent, any device)
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
-    if (err != hipSuccess) return err;
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-    if (wide)
-        hipLaunchKernelGGL(gemm_kernel<true>, grid, block, SMEM_BYTES, stream, a_codes, a_scales,
-                           w_codes, w_scales, M, N, K, c, ldc, out_scale, (int)tiles_m,
-                           (int)tiles_n);
-    else
-        hipLaunchKernelGGL(gemm_kernel<false>, grid, block, SMEM_BYTES, stream, a_codes, a_scales,
-                           w_codes, w_scales, M, N, K, c, ldc, out_scale, (int)tiles_m,
-                           (int)tiles_n);
-    return hipGetLastError();
+    return wide ? launch_tile<true>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
+                                    out_scale, tiles_m, tiles_n, stream)
+                : launch_tile<false>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
+                                     out_scale, tiles_m, tiles_n, stream);
 }
 
 }  // namespace if4
