@@ -5,31 +5,38 @@
 // from One Sign Bit", podcast companion page) routes each operand group by
 // its scale's sign bit to an FP or an INT decode path, with INT4 descaled by
 // 6/7 "during multiplication" (gist.science summary, section 2, "Metodo
-// 6/7").  Here each workgroup decodes its A and W K-slab once into LDS as
-// fp16 with the group scale folded in -- FP4 values c*s' exactly, INT4
-// values |q| * fl16(6 s'/7) -- and the waves run v_mfma_f32_32x32x16_f16
-// (one MFMA K-step = one IF4 group) with fp32 accumulation.  The per-tensor
-// 2^(E_A + E_W) is applied in the epilogue, so every decoded value stays in
-// fp16's normal range (2^-10 .. 2688).
+// 6/7").  Here both operands are decoded to fp16 with the group scale folded
+// in, and the waves run v_mfma_f32_32x32x16_f16 (one MFMA K-step = one IF4
+// group) with fp32 accumulation.
 //
-// Tiling: 256x256 output tile per workgroup of 4 waves (2 x 2), each wave
-// 128x128 (4 x 4 MFMA blocks of 32x32, 256 fp32 accumulators per lane in
-// AGPRs, one wave per SIMD).
-// K advances in slabs of 64 (four groups).  While the waves run the 64
-// MFMAs of slab s from one LDS buffer, every thread decodes its A row and
-// W row of slab s+1 into the other buffer, one group per 16-deep MFMA step,
-// and right after decoding a group reloads that group's registers with the
-// same group of slab s+2 -- so each load has a whole slab of MFMA work to
-// arrive in, with one register set and no copies.  One barrier per slab.
-// LDS: 2 buffers x 512 rows x 144 B (128 B of fp16 + 16 B pad, which spreads
-// the ds_read_b128/ds_write_b128 of consecutive rows over all banks).
-// Rows past M or N and groups past K load an in-range neighbour and decode
-// with a zero scale, so there are no branches around the loads.
+// Decode (decode_half): a code nibble becomes the high byte of an fp16
+// number by shifts and masks alone -- FP4 s.e1e0.m -> s.000e1e0.m (the fp16
+// value c * 2^-14; e = 0 lands on the fp16 subnormals, which keeps it
+// exact), INT4 s.mmm -> s.0000.mmm (|q| * 2^-16).  v_perm_b32 spreads four
+// such bytes into two fp16 pairs per instruction, and one packed fp16
+// multiply by the group multiplier -- s' * 2^5 for FP4, fl16(6 s' / 7) * 2^7
+// for INT4 -- gives every operand as (decoded value) * 2^-9.  FP4 operands
+// are exact; an INT4 operand is fl16(|q| * fl16(6 s'/7) * 2^-9), i.e. the
+// fp16 rounding of |q| * fl16(6 s'/7), with a 2^-15 absolute floor below
+// 2^-5.  The epilogue multiplies by 2^(E_A + E_W + 18).  fp16 subnormals
+// pass exactly through v_pk_mul_f16 and the MFMA on gfx950.
 //
-// Decode of one group is branch-free (the flag only picks a shift, a mask
-// and a power-of-two conversion scale): see decode_word.  A group lands in
-// LDS in the order 0,2,4,6,1,3,5,7 | 8,10,12,14,9,11,13,15; A and W use the
-// same order, so the dot products are unchanged.
+// Tiling: one 256x256 output tile per workgroup of 4 waves (one per SIMD).
+// Wave w owns A rows 64w..64w+63 of the tile and all 256 columns (2 x 8
+// MFMA blocks of 32x32, 256 fp32 accumulators per lane).  Because no other
+// wave needs those A rows, a wave decodes its A operand straight into MFMA
+// registers: lane l holds row l%32 and K-half l/32 of a 16-group, so a lane
+// loads 16 bytes of its row's 32-byte K slab and one v_permlane32_swap per
+// register pair hands each half-group to the lane that multiplies it.  The W
+// tile is shared by all four waves and goes through LDS: each thread decodes
+// one W row, 64 K values per slab, into a double-buffered 2 x 32 KB tile
+// laid out in MFMA fragment order (a wave reads a 32x16 fragment as one
+// contiguous 1 KB ds_read_b128).  While the MFMAs of K-slab s run, every
+// wave decodes slab s+1 (its A registers, one W row into the other LDS
+// buffer) and refills its load registers with slab s+2.  One barrier per
+// slab.  Rows past M or N load their nearest in-range row (those outputs
+// are never stored); groups past K (only without whole 64-deep slabs)
+// decode with a zero multiplier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,30 +50,18 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-// LDS tiles are stored in MFMA-fragment order: for each block of 32 rows,
-// each 16-deep group and each half of it, the 32 rows' 16-byte pieces lie
-// next to each other, so a wave reads a whole 32x16 fragment as one
-// contiguous 1 KB ds_read_b128 and a decoding wave writes contiguous 512 B
-// runs.  Offset of (row R, group g, half h) inside an operand tile:
-constexpr int TILE_BYTES = 256 * BK * 2;             // 32 KB per operand
-constexpr int BUF_BYTES = 2 * TILE_BYTES;            // A tile, then W tile
-constexpr int SMEM_BYTES = 2 * BUF_BYTES;            // double-buffered: 128 KB
+constexpr int kThreads = 256;
+constexpr int kGroups = BK / 16;                  // IF4 groups per K slab
+constexpr int TILE_BYTES = BN * BK * 2;           // decoded W slab: 32 KB
+constexpr int SMEM_BYTES = 2 * TILE_BYTES;        // double-buffered: 64 KB
+constexpr int FRAG_GROUP = 2 * 32 * 16;           // bytes between groups of a 32-row block
+constexpr int FRAG_BLOCK = kGroups * FRAG_GROUP;  // bytes between 32-row blocks
+// Offset of (row R, group g, half h) in the W tile: for each block of 32
+// rows, each group and each 8-value half, the 32 rows' 16-byte pieces are
+// contiguous.
 __device__ __forceinline__ int frag_off(int R, int g, int h) {
-    return ((((R >> 5) * (BK / 16) + g) * 2 + h) * 32 + (R & 31)) * 16;
+    return (R >> 5) * FRAG_BLOCK + g * FRAG_GROUP + h * 512 + (R & 31) * 16;
 }
-
-// Wave layout of a 256x256 tile: WM x WN waves, each (256/WM) x (256/WN).
-// With 4 waves every thread owns one A row and one W row; with 8 waves one
-// row of either.
-template <int WM, int WN>
-struct Layout {
-    static constexpr int kWaves = WM * WN;
-    static constexpr int kThreads = 64 * kWaves;
-    static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int FM = TM / 32, FN = TN / 32;
-    static constexpr bool kTwoRows = kThreads == BM;
-    static_assert(kThreads == BM || kThreads == BM + BN, "one or two rows per thread");
-};
 
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     half2v x = __builtin_bit_cast(half2v, a);
@@ -74,85 +69,71 @@ __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, x * y);
 }
 
-// One group's packed data in registers: 16 nibbles and the scale byte.  The
-// loaded values are only consumed by the decode one slab later, so nothing
-// may touch them right after the load (that would force a wait).
+// Group multiplier (both fp16 halves) and nibble shift from a scale byte.
+struct GroupScale {
+    uint32_t sig2;
+    uint32_t sh;
+};
+
+// s' comes from the hardware E4M3 conversion (exact; NaN for 0x7F, which
+// then poisons the group's products).  FP4: s' * 2^5 (exact in fp16);
+// INT4: fl16(fl32(s' * fl32(6/7))) * 2^7, computed as one fp32 product
+// (power-of-two factors do not change the roundings).
+__device__ __forceinline__ GroupScale group_scale(uint32_t b, bool zero) {
+    const float sp = __builtin_amdgcn_cvt_scalef32_f32_fp8(b & 0x7Fu, 1.0f, 0);
+    const bool int4 = (b & 0x80u) != 0;
+    float sig = sp * (int4 ? 0.857142866f * 128.0f : 32.0f);
+    sig = zero ? 0.0f : sig;
+    const uint32_t h16 = __builtin_bit_cast(uint16_t, (_Float16)sig);
+    GroupScale s;
+    s.sig2 = h16 | (h16 << 16);
+    s.sh = int4 ? 0u : 1u;
+    return s;
+}
+
+// Decode one code word (8 nibbles = half a group, element 2j in the low
+// nibble of byte j) into 8 fp16 operands in K order.
+__device__ __forceinline__ half8 decode_half(uint32_t w, GroupScale s) {
+    const uint32_t he = ((w & 0x07070707u) << s.sh) | ((w << 4) & 0x80808080u);
+    const uint32_t ho = (((w >> 4) & 0x07070707u) << s.sh) | (w & 0x80808080u);
+    // v_perm: byte j of `he` -> bits 15:8, byte j of `ho` -> bits 31:24, zeros below
+    uint4 o;
+    o.x = pk_mul(__builtin_amdgcn_perm(ho, he, 0x040C000Cu), s.sig2);
+    o.y = pk_mul(__builtin_amdgcn_perm(ho, he, 0x050C010Cu), s.sig2);
+    o.z = pk_mul(__builtin_amdgcn_perm(ho, he, 0x060C020Cu), s.sig2);
+    o.w = pk_mul(__builtin_amdgcn_perm(ho, he, 0x070C030Cu), s.sig2);
+    return __builtin_bit_cast(half8, o);
+}
+
+// One group's packed data in registers: 16 nibbles and the scale byte.
 struct Group {
     uint32_t w0, w1;
     uint32_t b;
 };
 
-// Decode one code word (8 nibbles) into 4 fp16 pairs.  Each nibble becomes
-// an E4M3 byte: FP4 s.e1e0.m -> s.00e1e0.m00, whose value is c * 2^-6; INT4
-// s.mmm -> s.0000.mmm, an E4M3 subnormal worth |q| * 2^-9.  The hardware
-// E4M3 -> fp16 conversion scales by 2^6 or 2^9 (exact), giving c or |q|, and
-// a packed fp16 multiply applies the group scale.  The even nibbles' bytes
-// and the odd nibbles' bytes are built in two words, so the pairs come out
-// as (0,2) (4,6) (1,3) (5,7).
-__device__ __forceinline__ void decode_word(uint32_t w, uint32_t sh, uint32_t rsh, uint32_t mask,
-                                            float cvt_scale, uint32_t sig2, uint32_t* out) {
-    const uint32_t ev = ((w << 4) & 0x80808080u) | ((w << sh) & mask);
-    const uint32_t od = (w & 0x80808080u) | ((w >> rsh) & mask);
-    out[0] = pk_mul(__builtin_bit_cast(uint32_t,
-                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, cvt_scale, false)), sig2);
-    out[1] = pk_mul(__builtin_bit_cast(uint32_t,
-                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, cvt_scale, true)), sig2);
-    out[2] = pk_mul(__builtin_bit_cast(uint32_t,
-                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, cvt_scale, false)), sig2);
-    out[3] = pk_mul(__builtin_bit_cast(uint32_t,
-                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, cvt_scale, true)), sig2);
-}
-
-// Decode a group to 16 fp16 values and store them (32 bytes) at dst.  The
-// group scale: s' from the E4M3 code by the hardware conversion (exact,
-// NaN for 0x7F), times fl32(6/7) for INT4, rounded once to fp16.
 __device__ __forceinline__ void decode_store(uint8_t* __restrict__ tile, int R, int gi,
                                              const Group& g, bool zero) {
-    const uint32_t b = g.b;
-    const float sp = __builtin_amdgcn_cvt_scalef32_f32_fp8(b & 0x7Fu, 1.0f, 0);
-    const bool int4 = (b & 0x80u) != 0;
-    float sig = int4 ? sp * 0.857142866f : sp;
-    sig = zero ? 0.0f : sig;
-    const uint32_t h16 = __builtin_bit_cast(uint16_t, (_Float16)sig);
-    const uint32_t sig2 = h16 | (h16 << 16);
-    const uint32_t sh = int4 ? 0u : 2u;
-    const uint32_t mask = 0x07070707u << sh;
-    const float cvt_scale = int4 ? 512.0f : 64.0f;
-    uint32_t h[8];
-    decode_word(g.w0, sh, 4u - sh, mask, cvt_scale, sig2, h);
-    decode_word(g.w1, sh, 4u - sh, mask, cvt_scale, sig2, h + 4);
-    *reinterpret_cast<uint4*>(tile + frag_off(R, gi, 0)) = make_uint4(h[0], h[1], h[2], h[3]);
-    *reinterpret_cast<uint4*>(tile + frag_off(R, gi, 1)) = make_uint4(h[4], h[5], h[6], h[7]);
+    const GroupScale s = group_scale(g.b, zero);
+    *reinterpret_cast<half8*>(tile + frag_off(R, gi, 0)) = decode_half(g.w0, s);
+    *reinterpret_cast<half8*>(tile + frag_off(R, gi, 1)) = decode_half(g.w1, s);
 }
 
-// Load group index gi (clamped into the row) of a row whose code and scale
-// rows start at cp and sp.  A group past K (or a row past M/N) decodes with
-// a zero scale, decided at decode time from the indices.
-__device__ __forceinline__ void load_group(const uint8_t* __restrict__ cp,
-                                           const uint8_t* __restrict__ sp, int64_t gi,
-                                           int64_t gpr, Group& g) {
-    const int64_t gc = gi < gpr ? gi : gpr - 1;
-    const uint2 q = *reinterpret_cast<const uint2*>(cp + gc * 8);
-    g.w0 = q.x;
-    g.w1 = q.y;
-    g.b = sp[gc];
-}
-
-// Slab register state of one row (A or W).  kWide: the slab's 32 code bytes
-// as two 16-byte words (groups 0-1, 2-3) and the 4 scale bytes as one word,
-// which needs 16-byte aligned code rows and K a multiple of 64; otherwise
-// one 8-byte word and one byte per group, clamped into the row.
+// W row state: the raw codes and scales of one 64-deep slab.  The loaded
+// values are only consumed one slab later, so nothing may touch them right
+// after the load (that would force a wait).  kWide: the slab's 32 code
+// bytes as two 16-byte words and the 4 scale bytes as one word (16-byte
+// aligned code rows and 4-byte aligned scale rows, K a multiple of 64);
+// otherwise one 8-byte word and one byte per group, clamped into the row.
 template <bool kWide>
-struct RowSlab;
+struct WRow;
 
 template <>
-struct RowSlab<true> {
+struct WRow<true> {
     uint4 c01, c23;
     uint32_t sw;
     uint32_t b[4];  // scale bytes of the slab being decoded
     __device__ __forceinline__ void start_decode() {
-        // take the scale bytes out first, so the scale word can be reloaded
-        // at once (it then has a whole slab to arrive)
+        // take the scale bytes out first so the scale word can be reloaded
 #pragma unroll
         for (int g = 0; g < 4; g++) b[g] = (sw >> (8 * g)) & 0xFFu;
     }
@@ -183,14 +164,19 @@ struct RowSlab<true> {
 };
 
 template <>
-struct RowSlab<false> {
+struct WRow<false> {
     Group gr[4];
     __device__ __forceinline__ void start_decode() {}
     __device__ __forceinline__ Group group(int g) const { return gr[g]; }
     __device__ __forceinline__ void refill(const uint8_t* __restrict__ cp,
                                            const uint8_t* __restrict__ sp, int64_t slab, int g,
                                            int64_t gpr) {
-        load_group(cp, sp, slab * 4 + g, gpr, gr[g]);
+        const int64_t gi = slab * 4 + g;
+        const int64_t gc = gi < gpr ? gi : gpr - 1;
+        const uint2 q = *reinterpret_cast<const uint2*>(cp + gc * 8);
+        gr[g].w0 = q.x;
+        gr[g].w1 = q.y;
+        gr[g].b = sp[gc];
     }
     __device__ __forceinline__ void load_all(const uint8_t* __restrict__ cp,
                                              const uint8_t* __restrict__ sp, int64_t slab,
@@ -200,21 +186,92 @@ struct RowSlab<false> {
     }
 };
 
-template <bool kWide, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN)
+// A state of one lane for its two 32-row blocks: the raw data of one slab,
+// and after take() the code word (group g, half lane/32) of each block with
+// the group's scale byte.
+template <bool kWide>
+struct ARows;
+
+template <>
+struct ARows<true> {
+    // lane l < 32 loads bytes 0-15 (groups 0-1) of its row's slab, lane
+    // l + 32 bytes 16-31 (groups 2-3); both load the slab's scale word
+    uint4 raw[2];
+    uint32_t rsw[2];
+    uint32_t word[2][4];
+    uint32_t sw[2];
+    __device__ __forceinline__ void load(const uint8_t* const* cp, const uint8_t* const* sp,
+                                         int64_t slab, int64_t gpr) {
+        (void)gpr;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            raw[i] = *reinterpret_cast<const uint4*>(cp[i] + slab * 32);
+            rsw[i] = *reinterpret_cast<const uint32_t*>(sp[i] + slab * 4);
+        }
+    }
+    // Lanes l and l + 32 trade halves: permlane32_swap(x, y) exchanges the
+    // upper 32 lanes of x with the lower 32 lanes of y, so words (0,1) of
+    // the 16 bytes become groups 0 and 2 and words (2,3) groups 1 and 3,
+    // each in the half that this lane multiplies.
+    __device__ __forceinline__ void take() {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const auto p = __builtin_amdgcn_permlane32_swap(raw[i].x, raw[i].y, false, false);
+            const auto q = __builtin_amdgcn_permlane32_swap(raw[i].z, raw[i].w, false, false);
+            word[i][0] = p[0];
+            word[i][2] = p[1];
+            word[i][1] = q[0];
+            word[i][3] = q[1];
+            sw[i] = rsw[i];
+        }
+    }
+    __device__ __forceinline__ uint32_t scale(int i, int g) const {
+        return (sw[i] >> (8 * g)) & 0xFFu;
+    }
+};
+
+template <>
+struct ARows<false> {
+    uint32_t raw[2][4];
+    uint32_t rb[2][4];
+    uint32_t word[2][4];
+    uint32_t sb[2][4];
+    int hoff;  // byte offset of this lane's half inside a group (0 or 4)
+    __device__ __forceinline__ void load(const uint8_t* const* cp, const uint8_t* const* sp,
+                                         int64_t slab, int64_t gpr) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int64_t gi = slab * 4 + g;
+                const int64_t gc = gi < gpr ? gi : gpr - 1;
+                raw[i][g] = *reinterpret_cast<const uint32_t*>(cp[i] + gc * 8 + hoff);
+                rb[i][g] = sp[i][gc];
+            }
+    }
+    __device__ __forceinline__ void take() {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                word[i][g] = raw[i][g];
+                sb[i][g] = rb[i][g];
+            }
+    }
+    __device__ __forceinline__ uint32_t scale(int i, int g) const { return sb[i][g]; }
+};
+
+template <bool kWide>
+__global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
             const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
             int64_t M, int64_t N, int64_t K, float* __restrict__ c, int64_t ldc, float out_scale,
             int tiles_m, int tiles_n) {
-    using LY = Layout<WM, WN>;
-    constexpr int TM = LY::TM, TN = LY::TN, FM = LY::FM, FN = LY::FN;
-    constexpr bool kTwo = LY::kTwoRows;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
 
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
     // contiguous run of tiles, walking down M within a column of W tiles so
@@ -224,128 +281,106 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     if (total % 8 == 0) bid = (bid % 8) * (total / 8) + bid / 8;
     const int tm = bid % tiles_m, tn = bid / tiles_m;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int64_t gpr = K / 16;
+    const int64_t kb = K / 2, gpr = K / 16;
 
-    // Rows this thread loads and decodes (clamped in range; dead rows decode
-    // to 0).  Row 0: A row tid (4 waves) or tile row tid of A-then-W (8
-    // waves); row 1 (4 waves only): W row tid.
-    const bool r0_is_w = !kTwo && tid >= BM;
-    const int lr0 = r0_is_w ? tid - BM : tid;
-    const int64_t g0row = (r0_is_w ? n0 : m0) + lr0;
-    const int64_t lim0 = r0_is_w ? N : M;
-    const bool dead0 = g0row >= lim0;
-    const int64_t cr0 = dead0 ? lim0 - 1 : g0row;
-    const uint8_t* const cp0 = (r0_is_w ? w_codes : a_codes) + cr0 * (K / 2);
-    const uint8_t* const sp0 = (r0_is_w ? w_scales : a_scales) + cr0 * gpr;
-    const int tile0 = r0_is_w ? TILE_BYTES : 0;  // operand tile of row 0
-    const int64_t wrow = n0 + tid;
-    const bool dead1 = wrow >= N;
-    const int64_t cr1 = dead1 ? N - 1 : wrow;
-    const uint8_t* const cp1 = w_codes + cr1 * (K / 2);
-    const uint8_t* const sp1 = w_scales + cr1 * gpr;
-    const int tile1 = TILE_BYTES;
+    // W row decoded by this thread (tile row tid)
+    const int64_t wrow = n0 + tid < N ? n0 + tid : N - 1;
+    const uint8_t* const wcp = w_codes + wrow * kb;
+    const uint8_t* const wsp = w_scales + wrow * gpr;
+    // A rows of this lane: row lane%32 of the wave's two 32-row blocks
+    const int half = lane >> 5;
+    const uint8_t* acp[2];
+    const uint8_t* asp[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int64_t r = m0 + 64 * wave + 32 * i + (lane & 31);
+        const int64_t rc = r < M ? r : M - 1;
+        acp[i] = a_codes + rc * kb + (kWide ? 16 * half : 0);
+        asp[i] = a_scales + rc * gpr;
+    }
 
-    float16v acc[FM][FN];
+    float16v acc[2][8];
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++)
+        for (int j = 0; j < 8; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     const int nslabs = (int)((K + BK - 1) / BK);
     const int64_t last = nslabs - 1;
-    RowSlab<kWide> r0, r1;
-    r0.load_all(cp0, sp0, 0, gpr);
-    if (kTwo) r1.load_all(cp1, sp1, 0, gpr);
-    r0.start_decode();
-    if (kTwo) r1.start_decode();
+    WRow<kWide> wr;
+    ARows<kWide> ar;
+    if constexpr (!kWide) ar.hoff = 4 * half;
+
+    // prologue: slab 0 decoded (W into buffer 0, A into registers), slab 1 loaded
+    wr.load_all(wcp, wsp, 0, gpr);
+    ar.load(acp, asp, 0, gpr);
+    wr.start_decode();
+    ar.take();
+    half8 a[2][kGroups];
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        decode_store(smem + tile0, lr0, g, r0.group(g), dead0 || g >= gpr);
-        if (kTwo) decode_store(smem + tile1, tid, g, r1.group(g), dead1 || g >= gpr);
+    for (int g = 0; g < kGroups; g++) {
+        const bool past = g >= gpr;
+        decode_store(smem, tid, g, wr.group(g), past);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            a[i][g] = decode_half(ar.word[i][g], group_scale(ar.scale(i, g), past));
     }
-    r0.load_all(cp0, sp0, last < 1 ? last : 1, gpr);
-    if (kTwo) r1.load_all(cp1, sp1, last < 1 ? last : 1, gpr);
+    wr.load_all(wcp, wsp, last < 1 ? last : 1, gpr);
+    ar.load(acp, asp, last < 1 ? last : 1, gpr);
     __syncthreads();
 
-    // fragment (block i, group kk) of this wave: frag_off(first row, kk, 0) + lane * 16
-    const int a_off = frag_off(wm * TM, 0, 0) + lane * 16;
-    const int w_off = TILE_BYTES + frag_off(wn * TN, 0, 0) + lane * 16;
-    constexpr int FRAG_BLOCK = (BK / 16) * 2 * 32 * 16;  // bytes between 32-row blocks
-    constexpr int FRAG_GROUP = 2 * 32 * 16;              // bytes between groups
-
-    // With two waves per SIMD (8 waves; waves w and w+4 share a SIMD) the
-    // pair runs in opposite phases inside every slab: one wave issues its
-    // MFMAs while its partner decodes, then they swap, so the matrix core
-    // and the VALU work at the same time.  With one wave per SIMD the decode
-    // is interleaved with the MFMAs instead.
-    const bool mfma_first = kTwo || wave < 4;
+    const int w_off = lane * 16;  // fragment (block j, group g) at j * FRAG_BLOCK + g * FRAG_GROUP
     for (int s = 0; s < nslabs; s++) {
-        const uint8_t* buf = smem + (s & 1) * BUF_BYTES;
-        uint8_t* nbuf = smem + ((s + 1) & 1) * BUF_BYTES;
+        const uint8_t* buf = smem + (s & 1) * TILE_BYTES;
+        uint8_t* nbuf = smem + ((s + 1) & 1) * TILE_BYTES;
         // registers hold slab s+1 (decoded now) and are refilled with slab
         // s+2, clamped: past the end the loads repeat the last slab and the
-        // decodes write a buffer nobody reads again
+        // decodes fill registers and a buffer that nobody reads again
         const int64_t sl = (int64_t)s + 2 < last ? (int64_t)s + 2 : last;
-        const int64_t gdec = (int64_t)(s + 1) * 4;  // first group decoded now
-        r0.start_decode();
-        if (kTwo) r1.start_decode();
-        auto decode_group = [&](int kk) {
-            const bool past = gdec + kk >= gpr;  // group of slab s+1 beyond K
-            decode_store(nbuf + tile0, lr0, kk, r0.group(kk), dead0 || past);
-            if (kTwo) decode_store(nbuf + tile1, tid, kk, r1.group(kk), dead1 || past);
-            r0.refill(cp0, sp0, sl, kk, gpr);
-            if (kTwo) r1.refill(cp1, sp1, sl, kk, gpr);
-        };
-        if (!mfma_first) {
+        const int64_t gdec = (int64_t)(s + 1) * kGroups;  // first group decoded now
+        wr.start_decode();
+        ar.take();
+        ar.load(acp, asp, sl, gpr);
+
+        half8 bv[2][8];
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; kk++) decode_group(kk);
-        }
-        half8 av[2][FM], bv[2][FN];
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            av[0][i] = *reinterpret_cast<const half8*>(buf + a_off + i * FRAG_BLOCK);
-#pragma unroll
-        for (int j = 0; j < FN; j++)
+        for (int j = 0; j < 8; j++)
             bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
+        for (int kk = 0; kk < kGroups; kk++) {
             const int cur = kk & 1;
-            if (kk + 1 < BK / 16) {
+            if (kk + 1 < kGroups) {
 #pragma unroll
-                for (int i = 0; i < FM; i++)
-                    av[cur ^ 1][i] = *reinterpret_cast<const half8*>(
-                        buf + a_off + i * FRAG_BLOCK + (kk + 1) * FRAG_GROUP);
-#pragma unroll
-                for (int j = 0; j < FN; j++)
+                for (int j = 0; j < 8; j++)
                     bv[cur ^ 1][j] = *reinterpret_cast<const half8*>(
                         buf + w_off + j * FRAG_BLOCK + (kk + 1) * FRAG_GROUP);
             }
 #pragma unroll
-            for (int i = 0; i < FM; i++)
+            for (int j = 0; j < 8; j++)
 #pragma unroll
-                for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j],
+                for (int i = 0; i < 2; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][kk], bv[cur][j],
                                                                        acc[i][j], 0, 0, 0);
-            if (kTwo) {
-                decode_group(kk);
-                // One MFMA (32 cycles in the matrix core), then a handful of
-                // VALU/LDS/global instructions.
+            // next slab, group kk: this wave's A operands and one W row
+            const bool past = gdec + kk >= gpr;
 #pragma unroll
-                for (int i = 0; i < FM * FN; i++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 2; i++)
+                a[i][kk] = decode_half(ar.word[i][kk], group_scale(ar.scale(i, kk), past));
+            decode_store(nbuf, tid, kk, wr.group(kk), past);
+            wr.refill(wcp, wsp, sl, kk, gpr);
+            // one MFMA (32 cycles in the matrix core), then a few VALU, LDS
+            // and global instructions
+#pragma unroll
+            for (int m = 0; m < 16; m++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+                if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                if (m == 4 || m == 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (m == 6) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global load
             }
-        }
-        if (!kTwo && mfma_first) {
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; kk++) decode_group(kk);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
@@ -353,14 +388,13 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // epilogue: lane holds column lane%32 of each 32x32 block, rows
     // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int64_t col = n0 + wn * TN + j * 32 + (lane & 31);
+        for (int j = 0; j < 8; j++) {
+            const int64_t col = n0 + j * 32 + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t row =
-                    m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (row < M && col < N) c[row * ldc + col] = acc[i][j][r] * out_scale;
             }
         }
@@ -373,25 +407,18 @@ __global__ void zero_kernel(float* __restrict__ c, int64_t M, int64_t N, int64_t
         c[(i / N) * ldc + (i % N)] = 0.0f;
 }
 
-
-#ifndef IF4_GEMM_WM
-#define IF4_GEMM_WM 4
-#define IF4_GEMM_WN 2
-#endif
-
 template <bool kWide>
 hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                        const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* c,
                        int64_t ldc, float out_scale, int64_t tiles_m, int64_t tiles_n,
                        hipStream_t stream) {
-    constexpr int WM = IF4_GEMM_WM, WN = IF4_GEMM_WN;
-    const void* fn = (const void*)gemm_kernel<kWide, WM, WN>;
-    // LDS above 64 KB must be requested per kernel (idempotent, any device)
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    // dynamic LDS limit for this kernel (idempotent, any device)
+    hipError_t err = hipFuncSetAttribute((const void*)gemm_kernel<kWide>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_kernel<kWide, WM, WN>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(Layout<WM, WN>::kThreads), SMEM_BYTES, stream, a_codes, a_scales,
-                       w_codes, w_scales, M, N, K, c, ldc, out_scale, (int)tiles_m, (int)tiles_n);
+    hipLaunchKernelGGL(gemm_kernel<kWide>, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads),
+                       SMEM_BYTES, stream, a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
+                       out_scale, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
@@ -408,8 +435,9 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t 
     }
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
-    // 2^(a_exp + w_exp), exact; |a_exp + w_exp| <= 128 is split in two factors
-    const int e = a_exp + w_exp;
+    // 2^(a_exp + w_exp + 18) (each decoded operand carries 2^-9), exact; the
+    // exponent lies in [-110, 146] and is split into two factors
+    const int e = a_exp + w_exp + 18;
     const float out_scale = pow2f(e / 2) * pow2f(e - e / 2);
     // Wide loads need 16-byte aligned code rows and 4-byte aligned scale rows
     // with whole 64-deep slabs.

@@ -7,7 +7,7 @@
 
 namespace if4 {
 
-// Power-of-two float 2^e for |e| <= 64 (exact).
+// Power-of-two float 2^e for -126 <= e <= 127 (exact).
 inline float pow2f(int e) {
     union {
         uint32_t u;

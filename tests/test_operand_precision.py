@@ -5,9 +5,10 @@ FP4 values c*s' have at most 6 significant bits and are exact in either
 types on a C4-shaped sample (activations with outlier columns, N(0, 0.02)
 weights, K = 4096), quantized by the oracle, against the exact fp64 product
 of the decoded operands, and checks the 1e-3 relative Frobenius budget.
-The fp16 simulation follows the kernel's decode exactly: FP4 c*s' exact,
-INT4 fl16(|q| * fl16(fl32(s' * fl32(6/7)))), products accumulated in fp64
-(the MFMA accumulates the exact fp16 products in fp32).
+The fp16 simulation follows the kernel's decode exactly: every operand is
+the decoded value times 2^-9 in fp16 (subnormals included), FP4 c*s' exact,
+INT4 fl16(|q| * fl16(fl32(s' * fl32(6/7))) * 2^-9); products accumulated in
+fp64 (the MFMA accumulates the exact fp16 products in fp32).
 """
 import numpy as np
 
@@ -35,8 +36,9 @@ def decode_kernel_fp16(codes, scales):
     sp = e4m3(b & 0x7F)
     int4 = (b & 0x80) != 0
     sig_int = (sp.astype(np.float32) * np.float32(6.0 / 7.0)).astype(np.float16)
-    v_int = (mag.astype(np.float16) * sig_int).astype(np.float16).astype(np.float64)
-    v_fp = (E2M1[mag] * sp).astype(np.float16).astype(np.float64)  # exact
+    v_int = (mag * sig_int.astype(np.float64) * 2.0**-9).astype(np.float16).astype(np.float64)
+    v_int = v_int * 2.0**9
+    v_fp = (E2M1[mag] * sp * 2.0**-9).astype(np.float16).astype(np.float64) * 2.0**9  # exact
     v = np.where(int4, v_int, v_fp)
     return np.where(neg == 1, -v, v)
 
