@@ -1,44 +1,10 @@
 // IF4 x IF4 (W4A4) GEMM for gfx950: C[M,N] = A[M,K] * W[N,K]^T, fp32 out.
 //
-// Both operands arrive packed (4-bit codes + one flagged E4M3 scale byte per
-// 16 values along K).  The pages' MAC unit ("MAC Unit: Decoding Two Formats
-// from One Sign Bit", podcast companion page) routes each operand group by
-// its scale's sign bit to an FP or an INT decode path, with INT4 descaled by
-// 6/7 "during multiplication" (gist.science summary, section 2, "Metodo
-// 6/7").  Here both operands are decoded to fp16 with the group scale folded
-// in, and the waves run v_mfma_f32_32x32x16_f16 (one MFMA K-step = one IF4
-// group) with fp32 accumulation.
-//
-// Decode (decode_half): a code nibble becomes the high byte of an fp16
-// number by shifts and masks alone -- FP4 s.e1e0.m -> s.000e1e0.m (the fp16
-// value c * 2^-14; e = 0 lands on the fp16 subnormals, which keeps it
-// exact), INT4 s.mmm -> s.0000.mmm (|q| * 2^-16).  v_perm_b32 spreads four
-// such bytes into two fp16 pairs per instruction, and one packed fp16
-// multiply by the group multiplier -- s' * 2^5 for FP4, fl16(6 s' / 7) * 2^7
-// for INT4 -- gives every operand as (decoded value) * 2^-9.  FP4 operands
-// are exact; an INT4 operand is fl16(|q| * fl16(6 s'/7) * 2^-9), i.e. the
-// fp16 rounding of |q| * fl16(6 s'/7), with a 2^-15 absolute floor below
-// 2^-5.  The epilogue multiplies by 2^(E_A + E_W + 18).  fp16 subnormals
-// pass exactly through v_pk_mul_f16 and the MFMA on gfx950.
-//
-// Tiling: one 256x256 output tile per workgroup of 4 waves (one per SIMD).
-// Wave w owns A rows 64w..64w+63 of the tile and all 256 columns (2 x 8
-// MFMA blocks of 32x32, 256 fp32 accumulators per lane).  Because no other
-// wave needs those A rows, a wave decodes its A operand straight into MFMA
-// registers: lane l holds row l%32 and K-half l/32 of a 16-group, so a lane
-// loads 16 bytes of its row's 32-byte K slab and one v_permlane32_swap per
-// register pair hands each half-group to the lane that multiplies it.  The W
-// tile is shared by all four waves and goes through LDS: each thread decodes
-// one W row, 64 K values per slab, into a double-buffered 2 x 32 KB tile
-// laid out in MFMA fragment order (a wave reads a 32x16 fragment as one
-// contiguous 1 KB ds_read_b128).  While the MFMAs of K-slab s run, every
-// wave decodes slab s+1 (its A registers, one W row into the other LDS
-// buffer) and refills its load registers with slab s+2.  One barrier per
-// slab.  Rows past M or N load their nearest in-range row (those outputs
-// are never stored); groups past K (only without whole 64-deep slabs)
-// decode with a zero multiplier.
+// (design notes: see the comment above gemm_kernel)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "if4_internal.h"
 
@@ -50,17 +16,35 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;                     // 4 waves, one per SIMD
 constexpr int kGroups = BK / 16;                  // IF4 groups per K slab
+constexpr int kWin = 4;                           // slabs per scale window (16 scale bytes)
 constexpr int TILE_BYTES = BN * BK * 2;           // decoded W slab: 32 KB
-constexpr int SMEM_BYTES = 2 * TILE_BYTES;        // double-buffered: 64 KB
-constexpr int FRAG_GROUP = 2 * 32 * 16;           // bytes between groups of a 32-row block
-constexpr int FRAG_BLOCK = kGroups * FRAG_GROUP;  // bytes between 32-row blocks
-// Offset of (row R, group g, half h) in the W tile: for each block of 32
-// rows, each group and each 8-value half, the 32 rows' 16-byte pieces are
-// contiguous.
-__device__ __forceinline__ int frag_off(int R, int g, int h) {
-    return (R >> 5) * FRAG_BLOCK + g * FRAG_GROUP + h * 512 + (R & 31) * 16;
+constexpr int LUT_OFF = 2 * TILE_BYTES;           // double-buffered W tile: 64 KB, then
+constexpr int LUT_ENTRIES = 257;                  // the scale table: 256 bytes + "zero"
+constexpr int SMEM_BYTES = LUT_OFF + LUT_ENTRIES * 8 + 8;
+constexpr int FRAG_STEP = 2 * 32 * 16;            // bytes between MFMA steps of a 32-row block
+constexpr int FRAG_BLOCK = kGroups * FRAG_STEP;   // bytes between 32-row blocks
+// MFMA step t (0..3) of a K slab multiplies, in lane half h (lanes 32h ..
+// 32h+31), the 8 values of word (group 2h + t/2, half t%2) of each row --
+// any assignment of the slab's 64 K indices to MFMA positions gives the same
+// sums as long as A and W use the same one, and this one lets an A lane use
+// the 16 bytes it loads (groups 2h, 2h+1) without trading data with other
+// lanes.  W tile offset of (row R, group g, half hf): for each block of 32
+// rows and each step, the fragment's 64 16-byte pieces are contiguous, so a
+// wave reads a fragment as one 1 KB ds_read_b128.
+__device__ __forceinline__ int frag_off(int R, int g, int hf) {
+    return (R >> 5) * FRAG_BLOCK + (2 * (g & 1) + hf) * FRAG_STEP + (g >> 1) * 512 +
+           (R & 31) * 16;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders
+// global memory, which makes every wave wait for its outstanding global
+// loads -- the prefetches of the next slabs -- at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
@@ -79,15 +63,32 @@ struct GroupScale {
 // then poisons the group's products).  FP4: s' * 2^5 (exact in fp16);
 // INT4: fl16(fl32(s' * fl32(6/7))) * 2^7, computed as one fp32 product
 // (power-of-two factors do not change the roundings).
-__device__ __forceinline__ GroupScale group_scale(uint32_t b, bool zero) {
+__device__ __forceinline__ GroupScale group_scale(uint32_t b) {
     const float sp = __builtin_amdgcn_cvt_scalef32_f32_fp8(b & 0x7Fu, 1.0f, 0);
     const bool int4 = (b & 0x80u) != 0;
-    float sig = sp * (int4 ? 0.857142866f * 128.0f : 32.0f);
-    sig = zero ? 0.0f : sig;
+    const float sig = sp * (int4 ? 0.857142866f * 128.0f : 32.0f);
     const uint32_t h16 = __builtin_bit_cast(uint16_t, (_Float16)sig);
     GroupScale s;
     s.sig2 = h16 | (h16 << 16);
     s.sh = int4 ? 0u : 1u;
+    return s;
+}
+
+// Every workgroup tabulates group_scale for the 256 scale bytes, plus entry
+// 256 = zero multiplier (groups past K), in LDS; a lookup is one
+// ds_read_b64 instead of a dozen VALU instructions.
+constexpr uint32_t kZeroScale = 256;
+__device__ __forceinline__ void fill_scale_table(uint8_t* smem, int tid) {
+    uint2* lut = reinterpret_cast<uint2*>(smem + LUT_OFF);
+    const GroupScale g = group_scale((uint32_t)tid);
+    lut[tid] = make_uint2(g.sig2, g.sh);
+    if (tid == 0) lut[kZeroScale] = make_uint2(0u, 1u);
+}
+__device__ __forceinline__ GroupScale lookup_scale(const uint8_t* smem, uint32_t idx) {
+    const uint2 v = reinterpret_cast<const uint2*>(smem + LUT_OFF)[idx];
+    GroupScale s;
+    s.sig2 = v.x;
+    s.sh = v.y;
     return s;
 }
 
@@ -105,162 +106,141 @@ __device__ __forceinline__ half8 decode_half(uint32_t w, GroupScale s) {
     return __builtin_bit_cast(half8, o);
 }
 
-// One group's packed data in registers: 16 nibbles and the scale byte.
-struct Group {
-    uint32_t w0, w1;
-    uint32_t b;
+// ---------------------------------------------------------------------------
+// Operand fetch.  The vector memory path costs about one cycle per distinct
+// cache line an instruction touches, so loads are shaped to touch few lines:
+// an A lane's 16 code bytes share their 32-byte row segment with its partner
+// lane (32 lines per instruction), two W lanes load the two halves of one
+// row's 32-byte slab (32 lines), and scale bytes are fetched 16 at a time,
+// four slabs' worth per row.
+//
+// kWide: 16-byte aligned code and scale rows, K a multiple of 256 (whole
+// scale windows).  Otherwise every word and byte is fetched on its own,
+// clamped into the row, and groups past K decode with a zero multiplier.
+
+// Codes of one slab for one lane: A blocks i = 0, 1 (row lane%32 of each,
+// groups 2h, 2h+1 with h = lane/32) and W rows k = 0, 1 (groups 2q, 2q+1
+// with q = lane%2).
+template <bool kWide>
+struct SlabCodes;
+
+template <>
+struct SlabCodes<true> {
+    uint4 a[2], w[2];
+    __device__ __forceinline__ void load(const uint8_t* const* acp, const uint8_t* const* asp,
+                                         const uint8_t* const* wcp, const uint8_t* const* wsp,
+                                         int64_t slab, int h, int q, int64_t gpr) {
+        (void)asp, (void)wsp, (void)h, (void)q, (void)gpr;
+#pragma unroll
+        for (int i = 0; i < 2; i++) a[i] = *reinterpret_cast<const uint4*>(acp[i] + slab * 32);
+#pragma unroll
+        for (int k = 0; k < 2; k++) w[k] = *reinterpret_cast<const uint4*>(wcp[k] + slab * 32);
+    }
+    // A block i, MFMA step t: word (group 2h + t/2, half t%2)
+    __device__ __forceinline__ uint32_t aword(int i, int t) const {
+        return t == 0 ? a[i].x : t == 1 ? a[i].y : t == 2 ? a[i].z : a[i].w;
+    }
+    // W row k, word u = 2 * (group - 2q) + half
+    __device__ __forceinline__ uint32_t wword(int k, int u) const {
+        return u == 0 ? w[k].x : u == 1 ? w[k].y : u == 2 ? w[k].z : w[k].w;
+    }
 };
 
-__device__ __forceinline__ void decode_store(uint8_t* __restrict__ tile, int R, int gi,
-                                             const Group& g, bool zero) {
-    const GroupScale s = group_scale(g.b, zero);
-    *reinterpret_cast<half8*>(tile + frag_off(R, gi, 0)) = decode_half(g.w0, s);
-    *reinterpret_cast<half8*>(tile + frag_off(R, gi, 1)) = decode_half(g.w1, s);
+template <>
+struct SlabCodes<false> {
+    uint32_t a[2][4], w[2][4];
+    uint32_t ab[2][4], wb[2][2];  // scale bytes
+    __device__ __forceinline__ void load(const uint8_t* const* acp, const uint8_t* const* asp,
+                                         const uint8_t* const* wcp, const uint8_t* const* wsp,
+                                         int64_t slab, int h, int q, int64_t gpr) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int64_t g = slab * kGroups + 2 * h + (t >> 1);
+                const int64_t gc = g < gpr ? g : gpr - 1;
+                a[i][t] = *reinterpret_cast<const uint32_t*>(acp[i] + gc * 8 + 4 * (t & 1));
+                ab[i][t] = asp[i][gc];
+            }
+#pragma unroll
+        for (int k = 0; k < 2; k++)
+#pragma unroll
+            for (int gg = 0; gg < 2; gg++) {
+                const int64_t g = slab * kGroups + 2 * q + gg;
+                const int64_t gc = g < gpr ? g : gpr - 1;
+                const uint2 v = *reinterpret_cast<const uint2*>(wcp[k] + gc * 8);
+                w[k][2 * gg] = v.x;
+                w[k][2 * gg + 1] = v.y;
+                wb[k][gg] = wsp[k][gc];
+            }
+    }
+    __device__ __forceinline__ uint32_t aword(int i, int t) const { return a[i][t]; }
+    __device__ __forceinline__ uint32_t wword(int k, int u) const { return w[k][u]; }
+};
+
+// Scale bytes of one 4-slab window (wide path): 16 bytes per A block row and
+// per W row; word u holds slab u's four groups.
+struct WinScales {
+    uint4 a[2], w[2];
+    __device__ __forceinline__ void load(const uint8_t* const* asp, const uint8_t* const* wsp,
+                                         int64_t win) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) a[i] = *reinterpret_cast<const uint4*>(asp[i] + win * 16);
+#pragma unroll
+        for (int k = 0; k < 2; k++) w[k] = *reinterpret_cast<const uint4*>(wsp[k] + win * 16);
+    }
+};
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
+    return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
 }
 
-// W row state: the raw codes and scales of one 64-deep slab.  The loaded
-// values are only consumed one slab later, so nothing may touch them right
-// after the load (that would force a wait).  kWide: the slab's 32 code
-// bytes as two 16-byte words and the 4 scale bytes as one word (16-byte
-// aligned code rows and 4-byte aligned scale rows, K a multiple of 64);
-// otherwise one 8-byte word and one byte per group, clamped into the row.
-template <bool kWide>
-struct WRow;
-
-template <>
-struct WRow<true> {
-    uint4 c01, c23;
-    uint32_t sw;
-    uint32_t b[4];  // scale bytes of the slab being decoded
-    __device__ __forceinline__ void start_decode() {
-        // take the scale bytes out first so the scale word can be reloaded
-#pragma unroll
-        for (int g = 0; g < 4; g++) b[g] = (sw >> (8 * g)) & 0xFFu;
-    }
-    __device__ __forceinline__ Group group(int g) const {
-        const uint4 c = g < 2 ? c01 : c23;
-        Group r;
-        r.w0 = (g & 1) ? c.z : c.x;
-        r.w1 = (g & 1) ? c.w : c.y;
-        r.b = b[g];
-        return r;
-    }
-    // reload after group g of the current slab was decoded
-    __device__ __forceinline__ void refill(const uint8_t* __restrict__ cp,
-                                           const uint8_t* __restrict__ sp, int64_t slab, int g,
-                                           int64_t gpr) {
-        (void)gpr;
-        if (g == 0) sw = *reinterpret_cast<const uint32_t*>(sp + slab * 4);
-        if (g == 1) c01 = reinterpret_cast<const uint4*>(cp + slab * 32)[0];
-        if (g == 3) c23 = reinterpret_cast<const uint4*>(cp + slab * 32)[1];
-    }
-    __device__ __forceinline__ void load_all(const uint8_t* __restrict__ cp,
-                                             const uint8_t* __restrict__ sp, int64_t slab,
-                                             int64_t gpr) {
-        refill(cp, sp, slab, 0, gpr);
-        refill(cp, sp, slab, 1, gpr);
-        refill(cp, sp, slab, 3, gpr);
-    }
-};
-
-template <>
-struct WRow<false> {
-    Group gr[4];
-    __device__ __forceinline__ void start_decode() {}
-    __device__ __forceinline__ Group group(int g) const { return gr[g]; }
-    __device__ __forceinline__ void refill(const uint8_t* __restrict__ cp,
-                                           const uint8_t* __restrict__ sp, int64_t slab, int g,
-                                           int64_t gpr) {
-        const int64_t gi = slab * 4 + g;
-        const int64_t gc = gi < gpr ? gi : gpr - 1;
-        const uint2 q = *reinterpret_cast<const uint2*>(cp + gc * 8);
-        gr[g].w0 = q.x;
-        gr[g].w1 = q.y;
-        gr[g].b = sp[gc];
-    }
-    __device__ __forceinline__ void load_all(const uint8_t* __restrict__ cp,
-                                             const uint8_t* __restrict__ sp, int64_t slab,
-                                             int64_t gpr) {
-#pragma unroll
-        for (int g = 0; g < 4; g++) refill(cp, sp, slab, g, gpr);
-    }
-};
-
-// A state of one lane for its two 32-row blocks: the raw data of one slab,
-// and after take() the code word (group g, half lane/32) of each block with
-// the group's scale byte.
-template <bool kWide>
-struct ARows;
-
-template <>
-struct ARows<true> {
-    // lane l < 32 loads bytes 0-15 (groups 0-1) of its row's slab, lane
-    // l + 32 bytes 16-31 (groups 2-3); both load the slab's scale word
-    uint4 raw[2];
-    uint32_t rsw[2];
-    uint32_t word[2][4];
-    uint32_t sw[2];
-    __device__ __forceinline__ void load(const uint8_t* const* cp, const uint8_t* const* sp,
-                                         int64_t slab, int64_t gpr) {
-        (void)gpr;
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            raw[i] = *reinterpret_cast<const uint4*>(cp[i] + slab * 32);
-            rsw[i] = *reinterpret_cast<const uint32_t*>(sp[i] + slab * 4);
-        }
-    }
-    // Lanes l and l + 32 trade halves: permlane32_swap(x, y) exchanges the
-    // upper 32 lanes of x with the lower 32 lanes of y, so words (0,1) of
-    // the 16 bytes become groups 0 and 2 and words (2,3) groups 1 and 3,
-    // each in the half that this lane multiplies.
-    __device__ __forceinline__ void take() {
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const auto p = __builtin_amdgcn_permlane32_swap(raw[i].x, raw[i].y, false, false);
-            const auto q = __builtin_amdgcn_permlane32_swap(raw[i].z, raw[i].w, false, false);
-            word[i][0] = p[0];
-            word[i][2] = p[1];
-            word[i][1] = q[0];
-            word[i][3] = q[1];
-            sw[i] = rsw[i];
-        }
-    }
-    __device__ __forceinline__ uint32_t scale(int i, int g) const {
-        return (sw[i] >> (8 * g)) & 0xFFu;
-    }
-};
-
-template <>
-struct ARows<false> {
-    uint32_t raw[2][4];
-    uint32_t rb[2][4];
-    uint32_t word[2][4];
-    uint32_t sb[2][4];
-    int hoff;  // byte offset of this lane's half inside a group (0 or 4)
-    __device__ __forceinline__ void load(const uint8_t* const* cp, const uint8_t* const* sp,
-                                         int64_t slab, int64_t gpr) {
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int64_t gi = slab * 4 + g;
-                const int64_t gc = gi < gpr ? gi : gpr - 1;
-                raw[i][g] = *reinterpret_cast<const uint32_t*>(cp[i] + gc * 8 + hoff);
-                rb[i][g] = sp[i][gc];
-            }
-    }
-    __device__ __forceinline__ void take() {
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                word[i][g] = raw[i][g];
-                sb[i][g] = rb[i][g];
-            }
-    }
-    __device__ __forceinline__ uint32_t scale(int i, int g) const { return sb[i][g]; }
-};
-
+// IF4 x IF4 GEMM kernel.
+//
+// Decode (decode_half): a code nibble becomes the high byte of an fp16
+// number by shifts and masks alone -- FP4 s.e1e0.m -> s.000e1e0.m (the fp16
+// value c * 2^-14; e = 0 lands on the fp16 subnormals, which keeps it
+// exact), INT4 s.mmm -> s.0000.mmm (|q| * 2^-16).  v_perm_b32 spreads four
+// such bytes into two fp16 pairs per instruction, and one packed fp16
+// multiply by the group multiplier -- s' * 2^5 for FP4, fl16(6 s' / 7) * 2^7
+// for INT4, looked up in a per-workgroup LDS table -- gives every operand as
+// (decoded value) * 2^-9.  FP4 operands are exact; an INT4 operand is
+// fl16(|q| * fl16(6 s'/7) * 2^-9), i.e. the fp16 rounding of
+// |q| * fl16(6 s'/7) with a 2^-15 absolute floor below 2^-5.  The epilogue
+// multiplies by 2^(E_A + E_W + 18).  fp16 subnormals pass exactly through
+// v_pk_mul_f16 and the MFMA on gfx950.  The scale's sign bit picks the
+// format per group (the pages' MAC unit: "MAC Unit: Decoding Two Formats
+// from One Sign Bit", podcast companion page; the 6/7 factor: gist.science
+// summary, section 2).
+//
+// Tiling: one 256x256 output tile per workgroup of 4 waves (one per SIMD);
+// wave w owns A rows 64w..64w+63 of the tile and all 256 columns (2 x 8
+// blocks of v_mfma_f32_32x32x16_f16, one MFMA K-step = one IF4 group,
+// 256 fp32 accumulators per lane).  No other wave needs those A rows, so a
+// wave decodes its A operand straight into MFMA registers: lane l holds row
+// l%32 and K-half l/32 of a 16-deep step.  MFMA step t (0..3) of a 64-deep K
+// slab multiplies, in lane half h, the 8 values of word (group 2h + t/2,
+// half t%2) of each row -- any assignment of the slab's 64 K indices to
+// MFMA positions gives the same sums as long as A and W use the same one,
+// and this one lets an A lane use the 16 bytes it loads as they are.  The W
+// tile is shared by the four waves and goes through LDS: each thread decodes
+// two groups of two W rows per slab into a double-buffered 2 x 32 KB tile
+// in MFMA fragment order (frag_off), which a wave reads as contiguous 1 KB
+// ds_read_b128s.
+//
+// Pipeline: while the MFMAs of K slab s run, each wave decodes slab s+1
+// (its A registers, its W share into the other LDS buffer) and fetches the
+// codes of slab s+2 into the register set that slab s used; scales arrive a
+// window ahead.  The slab loop is unrolled by the 4-slab window so that all
+// register sets are fixed and no loaded value is copied (a copy would wait
+// for its load).  One LDS-only barrier per slab.  Within a slab, each
+// MFMA step runs A block 0 against W blocks 0..7, then A block 1, in four
+// sub-blocks of four MFMAs; each sub-block carries one code-word decode
+// (about 16 VALU instructions) and the W fragment reads of the next step.
+// A block 0's operand of step t is replaced in sub-block 2 of step t, A
+// block 1's in sub-block 0 of step t+1 -- for the last step that is step 0
+// of the next slab, from a word kept across the barrier.  Rows past M or N
+// load their nearest in-range row (those outputs are never stored).
 template <bool kWide>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -283,20 +263,29 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t kb = K / 2, gpr = K / 16;
 
-    // W row decoded by this thread (tile row tid)
-    const int64_t wrow = n0 + tid < N ? n0 + tid : N - 1;
-    const uint8_t* const wcp = w_codes + wrow * kb;
-    const uint8_t* const wsp = w_scales + wrow * gpr;
     // A rows of this lane: row lane%32 of the wave's two 32-row blocks
-    const int half = lane >> 5;
+    const int h = lane >> 5, hs = 16 * h;
     const uint8_t* acp[2];
     const uint8_t* asp[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int64_t r = m0 + 64 * wave + 32 * i + (lane & 31);
         const int64_t rc = r < M ? r : M - 1;
-        acp[i] = a_codes + rc * kb + (kWide ? 16 * half : 0);
+        acp[i] = a_codes + rc * kb + (kWide ? 16 * h : 0);
         asp[i] = a_scales + rc * gpr;
+    }
+    // W rows of this thread: tile rows 64w + 32k + lane/2, groups 2q, 2q+1
+    const int q = lane & 1, qs = 16 * q;
+    int wr_row[2];
+    const uint8_t* wcp[2];
+    const uint8_t* wsp[2];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        wr_row[k] = 64 * wave + 32 * k + (lane >> 1);
+        const int64_t r = n0 + wr_row[k];
+        const int64_t rc = r < N ? r : N - 1;
+        wcp[k] = w_codes + rc * kb + (kWide ? 16 * q : 0);
+        wsp[k] = w_scales + rc * gpr;
     }
 
     float16v acc[2][8];
@@ -309,80 +298,156 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 
     const int nslabs = (int)((K + BK - 1) / BK);
     const int64_t last = nslabs - 1;
-    WRow<kWide> wr;
-    ARows<kWide> ar;
-    if constexpr (!kWide) ar.hoff = 4 * half;
+    const int64_t nwin = (nslabs + kWin - 1) / kWin;
 
-    // prologue: slab 0 decoded (W into buffer 0, A into registers), slab 1 loaded
-    wr.load_all(wcp, wsp, 0, gpr);
-    ar.load(acp, asp, 0, gpr);
-    wr.start_decode();
-    ar.take();
-    half8 a[2][kGroups];
+    fill_scale_table(smem, tid);
+    lds_barrier();
+
+    // Scale of A block i / W row k, group selected by t / gg, in slab
+    // `slab` = window slot u of a window's scales (wide) or from the slab's
+    // own bytes; groups past K exist only without whole slabs.
+    auto a_scale = [&](const SlabCodes<kWide>& x, const WinScales& win, int u, int64_t slab,
+                       int i, int t) {
+        uint32_t b;
+        if constexpr (kWide) {
+            b = (word_of(win.a[i], u) >> (hs + 8 * (t >> 1))) & 0xFFu;
+        } else {
+            const bool past = slab * kGroups + 2 * h + (t >> 1) >= gpr;
+            b = past ? kZeroScale : x.ab[i][t];
+        }
+        return lookup_scale(smem, b);
+    };
+    auto w_scale = [&](const SlabCodes<kWide>& x, const WinScales& win, int u, int64_t slab,
+                       int k, int gg) {
+        uint32_t b;
+        if constexpr (kWide) {
+            b = (word_of(win.w[k], u) >> (qs + 8 * gg)) & 0xFFu;
+        } else {
+            const bool past = slab * kGroups + 2 * q + gg >= gpr;
+            b = past ? kZeroScale : x.wb[k][gg];
+        }
+        return lookup_scale(smem, b);
+    };
+    // W row k, group 2q + gg, half hf into `tile`
+    auto w_store = [&](const SlabCodes<kWide>& x, GroupScale sc, int k, int gg, int hf,
+                       uint8_t* tile) {
+        *reinterpret_cast<half8*>(tile + frag_off(wr_row[k], 2 * q + gg, hf)) =
+            decode_half(x.wword(k, 2 * gg + hf), sc);
+    };
+
+    // register sets: raw[p] holds the codes of a slab of parity p
+    SlabCodes<kWide> raw[2];
+    WinScales win[2];      // scale windows: the running one and the next
+    half8 a[2][kGroups];   // decoded A operands [block][MFMA step] of the running slab
+    uint32_t w13;          // A block 1, last step: word and scale of the running slab
+    GroupScale s13;
+
+    // prologue: slab 0 decoded (W into buffer 0, A into registers), slab 1 fetched
+    if constexpr (kWide) {
+        win[0].load(asp, wsp, 0);
+        win[1].load(asp, wsp, nwin > 1 ? 1 : 0);
+    }
+    raw[0].load(acp, asp, wcp, wsp, 0, h, q, gpr);
+    raw[1].load(acp, asp, wcp, wsp, last < 1 ? last : 1, h, q, gpr);
 #pragma unroll
-    for (int g = 0; g < kGroups; g++) {
-        const bool past = g >= gpr;
-        decode_store(smem, tid, g, wr.group(g), past);
+    for (int t = 0; t < kGroups; t++) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
-            a[i][g] = decode_half(ar.word[i][g], group_scale(ar.scale(i, g), past));
+            a[i][t] = decode_half(raw[0].aword(i, t), a_scale(raw[0], win[0], 0, 0, i, t));
+        const int k = t >> 1, gg = t & 1;
+        const GroupScale sw = w_scale(raw[0], win[0], 0, 0, k, gg);
+        w_store(raw[0], sw, k, gg, 0, smem);
+        w_store(raw[0], sw, k, gg, 1, smem);
     }
-    wr.load_all(wcp, wsp, last < 1 ? last : 1, gpr);
-    ar.load(acp, asp, last < 1 ? last : 1, gpr);
-    __syncthreads();
+    w13 = raw[0].aword(1, kGroups - 1);
+    s13 = a_scale(raw[0], win[0], 0, 0, 1, kGroups - 1);
+    lds_barrier();
 
-    const int w_off = lane * 16;  // fragment (block j, group g) at j * FRAG_BLOCK + g * FRAG_GROUP
-    for (int s = 0; s < nslabs; s++) {
-        const uint8_t* buf = smem + (s & 1) * TILE_BYTES;
-        uint8_t* nbuf = smem + ((s + 1) & 1) * TILE_BYTES;
-        // registers hold slab s+1 (decoded now) and are refilled with slab
-        // s+2, clamped: past the end the loads repeat the last slab and the
-        // decodes fill registers and a buffer that nobody reads again
+    const int w_off = lane * 16;  // fragment (block j, step t) at j * FRAG_BLOCK + t * FRAG_STEP
+
+    // One slab s = s0 + U (s0 a multiple of 4): MFMAs of slab s from buffer
+    // U%2 while slab s+1 (register set (U+1)%2) is decoded into the other
+    // buffer and slab s+2 is fetched into set U%2.
+    auto slab_step = [&](auto UC, int s0, const WinScales& wcur, const WinScales& wnxt) {
+        constexpr int U = decltype(UC)::value;
+        constexpr int P = U & 1, Q = P ^ 1;
+        const int s = s0 + U;
+        const uint8_t* buf = smem + P * TILE_BYTES;
+        uint8_t* nbuf = smem + Q * TILE_BYTES;
+        const int64_t sn = (int64_t)s + 1;
+        // slab s+2, clamped: past the end the loads repeat the last slab and
+        // the decodes fill registers and a buffer that nobody reads again
         const int64_t sl = (int64_t)s + 2 < last ? (int64_t)s + 2 : last;
-        const int64_t gdec = (int64_t)(s + 1) * kGroups;  // first group decoded now
-        wr.start_decode();
-        ar.take();
-        ar.load(acp, asp, sl, gpr);
+        raw[P].load(acp, asp, wcp, wsp, sl, h, q, gpr);
+        // scales of slab s+1: slot U+1 of this window, or slot 0 of the next
+        const WinScales& sw_win = U + 1 < kWin ? wcur : wnxt;
+        constexpr int US = (U + 1) % kWin;
+        const SlabCodes<kWide>& x = raw[Q];
 
-        half8 bv[2][8];
+        half8 bv[8];
 #pragma unroll
         for (int j = 0; j < 8; j++)
-            bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
+            bv[j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
 #pragma unroll
-        for (int kk = 0; kk < kGroups; kk++) {
-            const int cur = kk & 1;
-            if (kk + 1 < kGroups) {
+        for (int t = 0; t < kGroups; t++) {
+            const int k = t >> 1, gg = t & 1;
+            const GroupScale sw = w_scale(x, sw_win, US, sn, k, gg);
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    bv[cur ^ 1][j] = *reinterpret_cast<const half8*>(
-                        buf + w_off + j * FRAG_BLOCK + (kk + 1) * FRAG_GROUP);
+            for (int sb = 0; sb < 4; sb++) {
+                const int i = sb >> 1;  // A block of this sub-block's MFMAs
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) {
+                    const int j = 4 * (sb & 1) + jj;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][t], bv[j], acc[i][j],
+                                                                       0, 0, 0);
+                    // last use of fragment j in this step: fetch the next step's
+                    if (i == 1 && t + 1 < kGroups)
+                        bv[j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK +
+                                                                (t + 1) * FRAG_STEP);
+                }
+                if (sb == 0) {
+                    if (t == 0)
+                        a[1][kGroups - 1] = decode_half(w13, s13);
+                    else
+                        a[1][t - 1] = decode_half(x.aword(1, t - 1),
+                                                  a_scale(x, sw_win, US, sn, 1, t - 1));
+                } else if (sb == 2) {
+                    a[0][t] = decode_half(x.aword(0, t), a_scale(x, sw_win, US, sn, 0, t));
+                } else {
+                    w_store(x, sw, k, gg, sb == 1 ? 0 : 1, nbuf);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    if (m == 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+                    if (m == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][kk], bv[cur][j],
-                                                                       acc[i][j], 0, 0, 0);
-            // next slab, group kk: this wave's A operands and one W row
-            const bool past = gdec + kk >= gpr;
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-                a[i][kk] = decode_half(ar.word[i][kk], group_scale(ar.scale(i, kk), past));
-            decode_store(nbuf, tid, kk, wr.group(kk), past);
-            wr.refill(wcp, wsp, sl, kk, gpr);
-            // one MFMA (32 cycles in the matrix core), then a few VALU, LDS
-            // and global instructions
-#pragma unroll
-            for (int m = 0; m < 16; m++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-                if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                if (m == 4 || m == 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                if (m == 6) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global load
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
+        w13 = x.aword(1, kGroups - 1);
+        s13 = a_scale(x, sw_win, US, sn, 1, kGroups - 1);
+        lds_barrier();
+    };
+
+    // One 4-slab window.  The scales of the window after next are fetched
+    // at its start, so that moving them into place at its end does not wait.
+    for (int s0 = 0; s0 < nslabs; s0 += kWin) {
+        WinScales nn;
+        if constexpr (kWide) {
+            const int64_t nw = (int64_t)s0 / kWin + 2;
+            nn.load(asp, wsp, nw < nwin ? nw : nwin - 1);
+        }
+        slab_step(std::integral_constant<int, 0>{}, s0, win[0], win[1]);
+        if (kWide || s0 + 1 < nslabs) slab_step(std::integral_constant<int, 1>{}, s0, win[0], win[1]);
+        if (kWide || s0 + 2 < nslabs) slab_step(std::integral_constant<int, 2>{}, s0, win[0], win[1]);
+        if (kWide || s0 + 3 < nslabs) slab_step(std::integral_constant<int, 3>{}, s0, win[0], win[1]);
+        if constexpr (kWide) {
+            win[0] = win[1];
+            win[1] = nn;
+        }
     }
 
     // epilogue: lane holds column lane%32 of each 32x32 block, rows
@@ -394,7 +459,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
             const int64_t col = n0 + j * 32 + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < M && col < N) c[row * ldc + col] = acc[i][j][r] * out_scale;
             }
         }
@@ -412,7 +477,7 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const ui
                        const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* c,
                        int64_t ldc, float out_scale, int64_t tiles_m, int64_t tiles_n,
                        hipStream_t stream) {
-    // dynamic LDS limit for this kernel (idempotent, any device)
+    // dynamic LDS above 64 KB must be allowed per kernel (idempotent, any device)
     hipError_t err = hipFuncSetAttribute((const void*)gemm_kernel<kWide>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
     if (err != hipSuccess) return err;
@@ -439,11 +504,11 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t 
     // exponent lies in [-110, 146] and is split into two factors
     const int e = a_exp + w_exp + 18;
     const float out_scale = pow2f(e / 2) * pow2f(e - e / 2);
-    // Wide loads need 16-byte aligned code rows and 4-byte aligned scale rows
-    // with whole 64-deep slabs.
-    const bool wide = K % 64 == 0 && (uintptr_t)a_codes % 16 == 0 &&
-                      (uintptr_t)w_codes % 16 == 0 && (uintptr_t)a_scales % 4 == 0 &&
-                      (uintptr_t)w_scales % 4 == 0;
+    // Wide fetches need 16-byte aligned code and scale rows and whole 4-slab
+    // scale windows.
+    const bool wide = K % (BK * kWin) == 0 && (uintptr_t)a_codes % 16 == 0 &&
+                      (uintptr_t)w_codes % 16 == 0 && (uintptr_t)a_scales % 16 == 0 &&
+                      (uintptr_t)w_scales % 16 == 0;
     return wide ? launch_tile<true>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
                                     out_scale, tiles_m, tiles_n, stream)
                 : launch_tile<false>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
