@@ -19,6 +19,7 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;                     // 4 waves, one per SIMD
 constexpr int kGroups = BK / 16;                  // IF4 groups per K slab
 constexpr int kWin = 4;                           // slabs per scale window (16 scale bytes)
+constexpr int kBandM = 4;                         // M-tiles per band of the tile order
 constexpr int TILE_BYTES = BN * BK * 2;           // decoded W slab: 32 KB
 constexpr int LUT_OFF = 2 * TILE_BYTES;           // double-buffered W tile: 64 KB, then
 constexpr int LUT_ENTRIES = 257;                  // the scale table: 256 bytes + "zero"
@@ -254,12 +255,19 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     const int wave = tid >> 6;
 
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-    // contiguous run of tiles, walking down M within a column of W tiles so
-    // that concurrently running tiles share W rows in their XCD's L2.
+    // contiguous run of tiles.  The run is ordered in bands of kBandM M-tiles:
+    // down a band, then across N, so that the 32 tiles an XCD runs at once
+    // (one per CU, in step along K) cover 4 x 8 tiles and share their A and
+    // W rows in the XCD's L2 -- 3072 distinct rows instead of the 8448 of a
+    // whole column of M-tiles.
     const int total = tiles_m * tiles_n;
     int bid = blockIdx.x;
     if (total % 8 == 0) bid = (bid % 8) * (total / 8) + bid / 8;
-    const int tm = bid % tiles_m, tn = bid / tiles_m;
+    const int band = bid / (kBandM * tiles_n);
+    const int first_m = band * kBandM;
+    const int band_m = tiles_m - first_m < kBandM ? tiles_m - first_m : kBandM;
+    const int in_band = bid - band * kBandM * tiles_n;
+    const int tm = first_m + in_band % band_m, tn = in_band / band_m;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t kb = K / 2, gpr = K / 16;
 
