@@ -15,6 +15,7 @@ fp16 MFMA peak, and the dequantize kernel timed after the step loop) are in
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -44,6 +45,30 @@ def quant_bytes(rows, cols, in_bytes=2):
 def dequant_bytes(rows, cols, out_bytes=2):
     n = rows * cols
     return n // 2 + n // 16 + n * out_bytes
+
+
+GEMM_SOURCE = os.path.join(ROOT, "adaptive_block_scaled_amd", "csrc", "gemm.hip")
+GEMM_HBM_PROFILE = os.path.join(ROOT, "profiles", "gemm_ffn_8192x28672x8192_hbm.txt")
+
+
+def measured_traffic(profile, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on other kernel source
+    (its `source_sha256` line no longer matches)."""
+    try:
+        fields = {}
+        with open(profile) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        with open(source, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("source_sha256") != digest:
+            return None
+        return int(fields["traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -158,7 +183,8 @@ def main():
     }
     roofline = {"kernel": "gemm", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(GEMM_HBM_PROFILE, GEMM_SOURCE)}
 
     cpu = None
     if not args.no_cpu_baseline:
