@@ -207,7 +207,7 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
 
     const int64_t ngroups = rows * gpr;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    auto group_ptr = [&](int64_t g) {
         int64_t off;
         if constexpr (kContig) {
             off = g * 16;
@@ -215,8 +215,9 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
             const int64_t r = g / gpr;
             off = r * ld_x + (g - r * gpr) * 16;
         }
-        const uint4* p = reinterpret_cast<const uint4*>(x + off);
-        const uint4 va = p[0], vb = p[1];
+        return reinterpret_cast<const uint4*>(x + off);
+    };
+    auto quantize_group = [&](const uint4 va, const uint4 vb, const int64_t g) {
         const uint32_t w[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
         float v[16];
 #pragma unroll
@@ -323,8 +324,39 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
         }
         *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(lo, hi);
         scales[g] = (uint8_t)byte;
+    };
+
+    // Each thread walks its groups with a stride of the whole grid (a few
+    // waves per SIMD); the next group's 32 input bytes are loaded while the
+    // current one is quantized, into the other of two register sets.
+    int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint4 a0 = make_uint4(0, 0, 0, 0), b0 = a0, a1 = a0, b1 = a0;
+    if (g < ngroups) {
+        const uint4* p = group_ptr(g);
+        a0 = p[0];
+        b0 = p[1];
+    }
+    for (; g < ngroups; g += 2 * stride) {
+        const int64_t g1 = g + stride;
+        if (g1 < ngroups) {
+            const uint4* p = group_ptr(g1);
+            a1 = p[0];
+            b1 = p[1];
+        }
+        quantize_group(a0, b0, g);
+        if (g1 >= ngroups) break;
+        if (g1 + stride < ngroups) {
+            const uint4* p = group_ptr(g1 + stride);
+            a0 = p[0];
+            b0 = p[1];
+        }
+        quantize_group(a1, b1, g1);
     }
 }
+
+#ifndef IF4_QUANT_BLOCKS
+#define IF4_QUANT_BLOCKS 8192
+#endif
 
 template <bool kBf16, int kMode>
 hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
@@ -332,7 +364,10 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
     const int64_t gpr = cols / 16;
     const int64_t ngroups = rows * gpr;
     int64_t blocks = (ngroups + kThreads - 1) / kThreads;
-    if (blocks > 65536) blocks = 65536;
+    // the bf16 kernel loops with prefetch: a few waves per SIMD suffice;
+    // the exact kernel keeps one group per thread where it can
+    const int64_t cap = kBf16 ? IF4_QUANT_BLOCKS : 65536;
+    if (blocks > cap) blocks = cap;
     const float pe = pow2f(scale_exp), pn = pow2f(-scale_exp);
     if constexpr (kBf16) {
         const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
