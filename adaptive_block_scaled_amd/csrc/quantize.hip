@@ -285,7 +285,9 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
             const float xa = __builtin_fabsf(v[i]);
             const float X = 7.0f * v[i];
             const float t = __builtin_fmaf(xa, k7, 48.0f);
-            const float r = __builtin_fminf(t + 12582864.0f, 12582919.0f);  // 1.5*2^23 + |q|
+            // 1.5*2^23 + |q|, clamped to |q| <= 7 (positive floats order as their bits)
+            const float r = __uint_as_float(
+                __builtin_elementwise_min(__float_as_uint(t + 12582864.0f), 0x4B400007u));
             rq[i] = __float_as_uint(r);
             const float q = r - 12582912.0f;
             const float df = __builtin_fmaf(-c[i], s7, X);

@@ -10,7 +10,9 @@ timed region.  `value` is the step's throughput counted as the GEMM's
 2*M*N*K flops per step time (TFLOP/s); per-kernel figures (quantize GB/s
 against the 8 TB/s HBM peak, GEMM TFLOP/s against the 2.5 PFLOP/s dense
 fp16 MFMA peak, and the dequantize kernel timed after the step loop) are in
-`kernels`, and `roofline` reports the dominant kernel.
+`kernels`, and `roofline` reports the dominant kernel.  `kernels` also
+holds a plain device-to-device copy of W's input, timed the same way, as the
+practical HBM reference for the memory-bound kernels (`frac_of_copy`).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -154,6 +156,21 @@ def main():
     torch.cuda.synchronize()
     ms_deq = ev_d[0].elapsed_time(ev_d[1]) / nd
 
+    # practical HBM reference: a plain device-to-device copy of W's bf16 input
+    # (reads and writes the same number of bytes), timed like the kernels
+    Wc = torch.empty_like(W)
+    for _ in range(2):
+        Wc.copy_(W)
+    ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_c[0].record()
+    for _ in range(nd):
+        Wc.copy_(W)
+    ev_c[1].record()
+    torch.cuda.synchronize()
+    copy_bytes = 2 * W.numel() * W.element_size()
+    copy_gbs = copy_bytes / (ev_c[0].elapsed_time(ev_c[1]) / nd * 1e-3) / 1e9
+    del Wc
+
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -172,14 +189,19 @@ def main():
 
     kernels = {
         "quantize_W": {"ms": round(ms_qw, 4), "bytes": qw_b, "GB/s": round(qw_gbs, 1),
-                        "frac_hbm_peak": round(qw_gbs / HBM_PEAK_GBS, 4)},
+                        "frac_hbm_peak": round(qw_gbs / HBM_PEAK_GBS, 4),
+                        "frac_of_copy": round(qw_gbs / copy_gbs, 4)},
         "quantize_A": {"ms": round(ms_qa, 4), "bytes": qa_b, "GB/s": round(qa_gbs, 1),
-                        "frac_hbm_peak": round(qa_gbs / HBM_PEAK_GBS, 4)},
+                        "frac_hbm_peak": round(qa_gbs / HBM_PEAK_GBS, 4),
+                        "frac_of_copy": round(qa_gbs / copy_gbs, 4)},
         "gemm": {"ms": round(ms_gemm, 4), "flop": flops, "TFLOP/s": round(gemm_tflops, 1),
                  "frac_mfma_peak": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
         "dequantize_A_bf16": {"ms": round(ms_deq, 4), "bytes": dequant_bytes(M, K),
                               "GB/s": round(deq_gbs, 1),
-                              "frac_hbm_peak": round(deq_gbs / HBM_PEAK_GBS, 4)},
+                              "frac_hbm_peak": round(deq_gbs / HBM_PEAK_GBS, 4),
+                              "frac_of_copy": round(deq_gbs / copy_gbs, 4)},
+        "hbm_copy_reference": {"bytes": copy_bytes, "GB/s": round(copy_gbs, 1),
+                               "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
     }
     roofline = {"kernel": "gemm", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
