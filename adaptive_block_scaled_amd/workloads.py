@@ -63,14 +63,25 @@ def hadamard16() -> np.ndarray:
     return h / 4.0  # orthonormal
 
 
+def rht16(x: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Per-group random-sign Hadamard rotation along dim 1: y_g = H (d * x_g)
+    with H the orthonormal 16x16 Sylvester matrix and d a vector of 16 signs
+    shared by all groups (fp32 numpy arithmetic)."""
+    rows, cols = x.shape
+    h = hadamard16().astype(np.float32)
+    g = x.reshape(rows, cols // GROUP, GROUP) * d
+    y = np.matmul(g, h.T)
+    return np.ascontiguousarray(y.reshape(rows, cols), dtype=np.float32)
+
+
+def random_signs(rng) -> np.ndarray:
+    return rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=GROUP)
+
+
 def rht_gradient(rows: int, cols: int, seed: int, sigma: float = 1e-3) -> np.ndarray:
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(sigma)
-    d = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=GROUP)
-    h = hadamard16().astype(np.float32)
-    g = x.reshape(rows, cols // GROUP, GROUP) * d
-    y = np.matmul(g, h.T)  # y_g = H (d * x_g), per group of 16 along dim 1
-    return np.ascontiguousarray(y.reshape(rows, cols), dtype=np.float32)
+    return rht16(x, random_signs(rng))
 
 
 def normal_weights(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarray:
