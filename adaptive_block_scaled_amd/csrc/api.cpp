@@ -30,6 +30,20 @@ int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
     return IF4_OK;
 }
 
+// x^T quantize: groups run along dim 0, so rows (not cols) must be whole
+// groups; x needs only element alignment (each lane loads single elements).
+int check_quantize_t(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                     const uint8_t* codes, const uint8_t* scales, int32_t scale_exp, int mode) {
+    if (x_dtype != IF4_F32 && x_dtype != IF4_BF16) return IF4_ERR_DTYPE;
+    if (mode < IF4_MODE_ADAPTIVE || mode > IF4_MODE_FORCE_INT4) return IF4_ERR_DTYPE;
+    if (rows < 0 || cols < 0 || rows % 16 != 0 || ld_x < cols) return IF4_ERR_SHAPE;
+    if (scale_exp < -kMaxExp || scale_exp > kMaxExp) return IF4_ERR_RANGE;
+    if (rows == 0 || cols == 0) return IF4_OK;
+    if (!x || !codes || !scales) return IF4_ERR_NULL;
+    if (!aligned(x, elem_size(x_dtype)) || !aligned(codes, 8)) return IF4_ERR_ALIGN;
+    return IF4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +70,15 @@ int if4_quantize_mode(const void* x, int x_dtype, int64_t rows, int64_t cols,
     if (st != IF4_OK || rows == 0 || cols == 0) return st;
     return hip_status(if4::launch_quantize(x, x_dtype == IF4_BF16, rows, cols, ld_x, codes,
                                            scales, scale_exp, mode, (hipStream_t)stream));
+}
+
+int if4_quantize_t(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                   int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                   int32_t scale_exp, int mode, void* stream) {
+    int st = check_quantize_t(x, x_dtype, rows, cols, ld_x, codes, scales, scale_exp, mode);
+    if (st != IF4_OK || rows == 0 || cols == 0) return st;
+    return hip_status(if4::launch_quantize_t(x, x_dtype == IF4_BF16, rows, cols, ld_x, codes,
+                                             scales, scale_exp, mode, (hipStream_t)stream));
 }
 
 int if4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,

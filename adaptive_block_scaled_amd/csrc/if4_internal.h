@@ -21,6 +21,10 @@ hipError_t launch_quantize(const void* x, int bf16, int64_t rows, int64_t cols,
                            int64_t ld_x, uint8_t* codes, uint8_t* scales,
                            int32_t scale_exp, int mode, hipStream_t stream);
 
+hipError_t launch_quantize_t(const void* x, int bf16, int64_t rows, int64_t cols,
+                             int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                             int32_t scale_exp, int mode, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
                              int64_t rows, int64_t cols, int32_t scale_exp,
                              void* y, int bf16, int64_t ld_y, hipStream_t stream);

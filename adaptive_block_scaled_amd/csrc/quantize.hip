@@ -104,6 +104,54 @@ __device__ __forceinline__ void load_group(const void* __restrict__ x, int64_t o
     }
 }
 
+// One group, exact rules for any fp32 values (x 2^-E): codes (element 2j in
+// the low nibble of byte j of lo:hi) and the flagged scale byte.
+template <int kMode>
+__device__ __forceinline__ void exact_group(const float (&v)[16], float p_exp, float p_negexp,
+                                            uint32_t& lo, uint32_t& hi, uint32_t& byte) {
+    // group absmax; a NaN or infinity anywhere makes the group non-finite
+    float a = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        float ax = __builtin_fabsf(v[i]);
+        finite &= ax <= 3.40282347e38f;
+        a = __builtin_fmaxf(a, ax);
+    }
+    uint32_t sc = scale_code(a * p_negexp);
+    lo = 0, hi = 0, byte = 0;
+    if (!finite) {
+        byte = 0x7Fu;
+    } else if (sc != 0) {
+        const float s = e4m3_value(sc) * p_exp;
+        const float s7 = 7.0f * s, s6 = 6.0f * s, t3 = 3.0f * s;
+        float ef = 0.0f, ei = 0.0f;
+        uint32_t fl = 0, fh = 0, il = 0, ih = 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float ax = __builtin_fabsf(v[i]);
+            const uint32_t fi = fp4_index(ax, s);
+            const uint32_t qi = int4_mag(ax, t3);
+            const float df = __builtin_fmaf(ax, 7.0f, -(e2m1_value(fi) * s7));
+            const float di = __builtin_fmaf(ax, 7.0f, -((float)qi * s6));
+            ef = __builtin_fmaf(df, df, ef);
+            ei = __builtin_fmaf(di, di, ei);
+            const uint32_t sg = (__float_as_uint(v[i]) >> 28) & 8u;
+            if (i < 8) {
+                fl |= (sg | fi) << (4 * i);
+                il |= (sg | qi) << (4 * i);
+            } else {
+                fh |= (sg | fi) << (4 * (i - 8));
+                ih |= (sg | qi) << (4 * (i - 8));
+            }
+        }
+        const bool use_int4 = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
+        lo = use_int4 ? il : fl;
+        hi = use_int4 ? ih : fh;
+        byte = sc | (use_int4 ? 0x80u : 0u);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Exact reference path (any fp32 input): thresholds compared exactly.
 template <bool kBf16, int kMode>
@@ -119,47 +167,8 @@ quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int
         float v[16];
         load_group<kBf16>(x, r * ld_x + cg * 16, v);
 
-        // group absmax; a NaN or infinity anywhere makes the group non-finite
-        float a = 0.0f;
-        bool finite = true;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            float ax = __builtin_fabsf(v[i]);
-            finite &= ax <= 3.40282347e38f;
-            a = __builtin_fmaxf(a, ax);
-        }
-        uint32_t sc = scale_code(a * p_negexp);
-        uint32_t lo = 0, hi = 0, byte = 0;
-        if (!finite) {
-            byte = 0x7Fu;
-        } else if (sc != 0) {
-            const float s = e4m3_value(sc) * p_exp;
-            const float s7 = 7.0f * s, s6 = 6.0f * s, t3 = 3.0f * s;
-            float ef = 0.0f, ei = 0.0f;
-            uint32_t fl = 0, fh = 0, il = 0, ih = 0;
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const float ax = __builtin_fabsf(v[i]);
-                const uint32_t fi = fp4_index(ax, s);
-                const uint32_t qi = int4_mag(ax, t3);
-                const float df = __builtin_fmaf(ax, 7.0f, -(e2m1_value(fi) * s7));
-                const float di = __builtin_fmaf(ax, 7.0f, -((float)qi * s6));
-                ef = __builtin_fmaf(df, df, ef);
-                ei = __builtin_fmaf(di, di, ei);
-                const uint32_t sg = (__float_as_uint(v[i]) >> 28) & 8u;
-                if (i < 8) {
-                    fl |= (sg | fi) << (4 * i);
-                    il |= (sg | qi) << (4 * i);
-                } else {
-                    fh |= (sg | fi) << (4 * (i - 8));
-                    ih |= (sg | qi) << (4 * (i - 8));
-                }
-            }
-            const bool use_int4 = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
-            lo = use_int4 ? il : fl;
-            hi = use_int4 ? ih : fh;
-            byte = sc | (use_int4 ? 0x80u : 0u);
-        }
+        uint32_t lo, hi, byte;
+        exact_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
         *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(lo, hi);
         scales[g] = (uint8_t)byte;
     }
@@ -188,12 +197,9 @@ quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int
 //    fp32, so fma(-c, 7s, 7x) equals the reference fma(|x|, 7, -|c|*7s).
 //  * non-finite: a NaN reaches the FP4 error sum (NaN) and an infinity the
 //    absmax; zero-scale groups use a zero reciprocal so their sums stay finite.
-template <int kMode, bool kContig>
-__global__ void __launch_bounds__(kThreads)
-quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
-                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
-                     float p_negexp) {
-    __shared__ float2 recip[128];  // (RN(1/s'), RN(7/(6 s'))) per scale code; 0 for code 0
+// Per-workgroup table of (RN(1/s'), RN(7/(6 s'))) per scale code; 0 for
+// code 0 (and the unused NaN code), so zero-scale groups stay finite.
+__device__ __forceinline__ void fill_recip(float2* recip) {
     if (threadIdx.x < 128) {
         const uint32_t c = threadIdx.x;
         float2 t = make_float2(0.0f, 0.0f);
@@ -203,6 +209,122 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
         }
         recip[c] = t;
     }
+}
+
+// One group of bf16-exact values, fast path (see above): codes and flagged
+// scale byte, identical to exact_group for bf16 inputs.
+template <int kMode>
+__device__ __forceinline__ void fast_group(const float (&v)[16], const float2* recip,
+                                           float p_exp, float p_negexp, uint32_t& lo,
+                                           uint32_t& hi, uint32_t& byte) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+
+    // scale code: RNE_E4M3(a * 2^-E / 6), saturating at 448
+    const float q6 = (a * p_negexp) * 0.16666667f;
+    uint32_t sc;
+    if (q6 < 0.015625f) {
+        sc = (uint32_t)__builtin_rintf(q6 * 512.0f);
+    } else {
+        uint32_t b = __float_as_uint(q6);
+        b = b + 0x7FFFFu + ((b >> 20) & 1u);
+        sc = (b >> 20) - 960u;
+        sc = sc < 0x7Eu ? sc : 0x7Eu;
+    }
+    const float s = e4m3_value(sc) * p_exp;
+    const float2 rc = recip[sc];
+    const float inv_s = rc.x * p_negexp, k7 = rc.y * p_negexp;
+    const float s7 = 7.0f * s, s6 = 6.0f * s;
+
+    // FP4 codes via the hardware E2M1 conversion of the snapped quotients
+    float us[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float t = __builtin_fmaf(__builtin_fabsf(v[i]), inv_s, 48.0f) - 48.0f;
+        us[i] = __builtin_copysignf(t, v[i]);
+    }
+    uint32_t f0 = 0, f1 = 0;
+    f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[0], us[1], 1.0f, 0);
+    f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[2], us[3], 1.0f, 1);
+    f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[4], us[5], 1.0f, 2);
+    f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[6], us[7], 1.0f, 3);
+    f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[8], us[9], 1.0f, 0);
+    f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[10], us[11], 1.0f, 1);
+    f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[12], us[13], 1.0f, 2);
+    f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[14], us[15], 1.0f, 3);
+    float c[16];
+    {
+        auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 0);
+        auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 1);
+        auto d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 2);
+        auto d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 3);
+        auto d4 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 0);
+        auto d5 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 1);
+        auto d6 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 2);
+        auto d7 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 3);
+        c[0] = d0[0]; c[1] = d0[1]; c[2] = d1[0]; c[3] = d1[1];
+        c[4] = d2[0]; c[5] = d2[1]; c[6] = d3[0]; c[7] = d3[1];
+        c[8] = d4[0]; c[9] = d4[1]; c[10] = d5[0]; c[11] = d5[1];
+        c[12] = d6[0]; c[13] = d6[1]; c[14] = d7[0]; c[15] = d7[1];
+    }
+
+    // INT4 magnitudes and both error sums, index order 0..15
+    float ef = 0.0f, ei = 0.0f;
+    uint32_t rq[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float xa = __builtin_fabsf(v[i]);
+        const float X = 7.0f * v[i];
+        const float t = __builtin_fmaf(xa, k7, 48.0f);
+        // 1.5*2^23 + |q|, clamped to |q| <= 7 (positive floats order as their bits)
+        const float r = __uint_as_float(
+            __builtin_elementwise_min(__float_as_uint(t + 12582864.0f), 0x4B400007u));
+        rq[i] = __float_as_uint(r);
+        const float q = r - 12582912.0f;
+        const float df = __builtin_fmaf(-c[i], s7, X);
+        const float di = __builtin_fmaf(-q, s6, __builtin_fabsf(X));
+        ef = __builtin_fmaf(df, df, ef);
+        ei = __builtin_fmaf(di, di, ei);
+    }
+    // gather |q| (low byte of each float) into nibbles: even elements in
+    // bits 0-2, odd elements in bits 4-6 of each byte
+    uint32_t i0, i1;
+    {
+        const uint32_t e0 = __builtin_amdgcn_perm(rq[2], rq[0], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(rq[6], rq[4], 0x04000C0Cu);
+        const uint32_t o0 = __builtin_amdgcn_perm(rq[3], rq[1], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(rq[7], rq[5], 0x04000C0Cu);
+        const uint32_t e1 = __builtin_amdgcn_perm(rq[10], rq[8], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(rq[14], rq[12], 0x04000C0Cu);
+        const uint32_t o1 = __builtin_amdgcn_perm(rq[11], rq[9], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(rq[15], rq[13], 0x04000C0Cu);
+        // sign bits are those of the FP4 codes (both take x's sign bit)
+        i0 = (e0 | (o0 << 4)) | (f0 & 0x88888888u);
+        i1 = (e1 | (o1 << 4)) | (f1 & 0x88888888u);
+    }
+
+    const bool use_int4 = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
+    lo = use_int4 ? i0 : f0;
+    hi = use_int4 ? i1 : f1;
+    byte = sc | (use_int4 ? 0x80u : 0u);
+    if (sc == 0) {
+        lo = hi = 0;
+        byte = 0;
+    }
+    if (!(a <= 3.40282347e38f) || ef != ef) {  // infinity or NaN in the group
+        lo = hi = 0;
+        byte = 0x7Fu;
+    }
+}
+
+template <int kMode, bool kContig>
+__global__ void __launch_bounds__(kThreads)
+quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
+                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
+                     float p_negexp) {
+    __shared__ float2 recip[128];
+    fill_recip(recip);
     __syncthreads();
 
     const int64_t ngroups = rows * gpr;
@@ -225,105 +347,8 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
             v[2 * i] = __uint_as_float(w[i] << 16);
             v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
-        float a = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-
-        // scale code: RNE_E4M3(a * 2^-E / 6), saturating at 448
-        const float q6 = (a * p_negexp) * 0.16666667f;
-        uint32_t sc;
-        if (q6 < 0.015625f) {
-            sc = (uint32_t)__builtin_rintf(q6 * 512.0f);
-        } else {
-            uint32_t b = __float_as_uint(q6);
-            b = b + 0x7FFFFu + ((b >> 20) & 1u);
-            sc = (b >> 20) - 960u;
-            sc = sc < 0x7Eu ? sc : 0x7Eu;
-        }
-        const float s = e4m3_value(sc) * p_exp;
-        const float2 rc = recip[sc];
-        const float inv_s = rc.x * p_negexp, k7 = rc.y * p_negexp;
-        const float s7 = 7.0f * s, s6 = 6.0f * s;
-
-        // FP4 codes via the hardware E2M1 conversion of the snapped quotients
-        float us[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const float t = __builtin_fmaf(__builtin_fabsf(v[i]), inv_s, 48.0f) - 48.0f;
-            us[i] = __builtin_copysignf(t, v[i]);
-        }
-        uint32_t f0 = 0, f1 = 0;
-        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[0], us[1], 1.0f, 0);
-        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[2], us[3], 1.0f, 1);
-        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[4], us[5], 1.0f, 2);
-        f0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f0, us[6], us[7], 1.0f, 3);
-        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[8], us[9], 1.0f, 0);
-        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[10], us[11], 1.0f, 1);
-        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[12], us[13], 1.0f, 2);
-        f1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f1, us[14], us[15], 1.0f, 3);
-        float c[16];
-        {
-            auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 0);
-            auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 1);
-            auto d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 2);
-            auto d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f0, 1.0f, 3);
-            auto d4 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 0);
-            auto d5 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 1);
-            auto d6 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 2);
-            auto d7 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f1, 1.0f, 3);
-            c[0] = d0[0]; c[1] = d0[1]; c[2] = d1[0]; c[3] = d1[1];
-            c[4] = d2[0]; c[5] = d2[1]; c[6] = d3[0]; c[7] = d3[1];
-            c[8] = d4[0]; c[9] = d4[1]; c[10] = d5[0]; c[11] = d5[1];
-            c[12] = d6[0]; c[13] = d6[1]; c[14] = d7[0]; c[15] = d7[1];
-        }
-
-        // INT4 magnitudes and both error sums, index order 0..15
-        float ef = 0.0f, ei = 0.0f;
-        uint32_t rq[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const float xa = __builtin_fabsf(v[i]);
-            const float X = 7.0f * v[i];
-            const float t = __builtin_fmaf(xa, k7, 48.0f);
-            // 1.5*2^23 + |q|, clamped to |q| <= 7 (positive floats order as their bits)
-            const float r = __uint_as_float(
-                __builtin_elementwise_min(__float_as_uint(t + 12582864.0f), 0x4B400007u));
-            rq[i] = __float_as_uint(r);
-            const float q = r - 12582912.0f;
-            const float df = __builtin_fmaf(-c[i], s7, X);
-            const float di = __builtin_fmaf(-q, s6, __builtin_fabsf(X));
-            ef = __builtin_fmaf(df, df, ef);
-            ei = __builtin_fmaf(di, di, ei);
-        }
-        // gather |q| (low byte of each float) into nibbles: even elements in
-        // bits 0-2, odd elements in bits 4-6 of each byte
-        uint32_t i0, i1;
-        {
-            const uint32_t e0 = __builtin_amdgcn_perm(rq[2], rq[0], 0x0C0C0400u) |
-                                __builtin_amdgcn_perm(rq[6], rq[4], 0x04000C0Cu);
-            const uint32_t o0 = __builtin_amdgcn_perm(rq[3], rq[1], 0x0C0C0400u) |
-                                __builtin_amdgcn_perm(rq[7], rq[5], 0x04000C0Cu);
-            const uint32_t e1 = __builtin_amdgcn_perm(rq[10], rq[8], 0x0C0C0400u) |
-                                __builtin_amdgcn_perm(rq[14], rq[12], 0x04000C0Cu);
-            const uint32_t o1 = __builtin_amdgcn_perm(rq[11], rq[9], 0x0C0C0400u) |
-                                __builtin_amdgcn_perm(rq[15], rq[13], 0x04000C0Cu);
-            // sign bits are those of the FP4 codes (both take x's sign bit)
-            i0 = (e0 | (o0 << 4)) | (f0 & 0x88888888u);
-            i1 = (e1 | (o1 << 4)) | (f1 & 0x88888888u);
-        }
-
-        const bool use_int4 = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
-        uint32_t lo = use_int4 ? i0 : f0;
-        uint32_t hi = use_int4 ? i1 : f1;
-        uint32_t byte = sc | (use_int4 ? 0x80u : 0u);
-        if (sc == 0) {
-            lo = hi = 0;
-            byte = 0;
-        }
-        if (!(a <= 3.40282347e38f) || ef != ef) {  // infinity or NaN in the group
-            lo = hi = 0;
-            byte = 0x7Fu;
-        }
+        uint32_t lo, hi, byte;
+        fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
         *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(lo, hi);
         scales[g] = (uint8_t)byte;
     };
@@ -386,6 +411,76 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Quantize of x^T: groups are 16 consecutive rows of one column of x, and
+// the output is the IF4 encoding of x^T ([cols, rows] row-major: codes
+// [cols, rows/2], scales [cols, rows/16]) -- the operand layout the backward
+// GEMMs of W4A4G4 training need (dgrad groups W along N, wgrad groups dY and
+// X along M).  Same per-group arithmetic as the row kernels.  A workgroup
+// owns 256 consecutive columns (one per lane) and a chunk of kTChunk
+// row-groups: each of a group's 16 loads reads 64 consecutive columns of one
+// row (coalesced), and each lane writes its column's codes for consecutive
+// row-groups, filling whole 128-byte lines.  The next group's 16 values are
+// loaded while the current one is quantized.
+constexpr int kTChunk = 16;
+
+template <bool kBf16, int kMode>
+__global__ void __launch_bounds__(kThreads)
+quantize_t_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
+                  float p_negexp, int64_t col_blocks) {
+    __shared__ float2 recip[128];
+    if constexpr (kBf16) {
+        fill_recip(recip);
+        __syncthreads();
+    }
+    const int64_t cb = blockIdx.x % col_blocks, chunk = blockIdx.x / col_blocks;
+    const int64_t col = cb * kThreads + threadIdx.x;
+    const int64_t rgs = rows / 16;
+    const int64_t rg0 = chunk * kTChunk;
+    const int64_t rg1 = rg0 + kTChunk < rgs ? rg0 + kTChunk : rgs;
+    if (col >= cols) return;
+
+    uint32_t raw[16];
+    auto load = [&](int64_t rg) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int64_t off = (rg * 16 + i) * ld_x + col;
+            if constexpr (kBf16)
+                raw[i] = reinterpret_cast<const uint16_t*>(x)[off];
+            else
+                raw[i] = reinterpret_cast<const uint32_t*>(x)[off];
+        }
+    };
+    load(rg0);
+    for (int64_t rg = rg0; rg < rg1; rg++) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = __uint_as_float(kBf16 ? raw[i] << 16 : raw[i]);
+        if (rg + 1 < rg1) load(rg + 1);
+        uint32_t lo, hi, byte;
+        if constexpr (kBf16)
+            fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
+        else
+            exact_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
+        *reinterpret_cast<uint2*>(codes + col * (rows / 2) + rg * 8) = make_uint2(lo, hi);
+        scales[col * rgs + rg] = (uint8_t)byte;
+    }
+}
+
+template <bool kBf16, int kMode>
+hipError_t launch_t(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                    uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
+    const int64_t col_blocks = (cols + kThreads - 1) / kThreads;
+    const int64_t chunks = (rows / 16 + kTChunk - 1) / kTChunk;
+    if (col_blocks * chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quantize_t_kernel<kBf16, kMode>), dim3((unsigned)(col_blocks * chunks)),
+                       dim3(kThreads), 0, stream, x, rows, cols, ld_x, codes, scales,
+                       pow2f(scale_exp), pow2f(-scale_exp), col_blocks);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ld_x,
@@ -399,6 +494,23 @@ hipError_t launch_quantize(const void* x, int bf16, int64_t rows, int64_t cols, 
     if (mode == 1) return launch<false, 1>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
     if (mode == 2) return launch<false, 2>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
     return launch<false, 0>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+}
+
+}  // namespace if4
+
+namespace if4 {
+
+hipError_t launch_quantize_t(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t* codes, uint8_t* scales, int32_t scale_exp, int mode,
+                             hipStream_t stream) {
+    if (bf16) {
+        if (mode == 1) return launch_t<true, 1>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+        if (mode == 2) return launch_t<true, 2>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+        return launch_t<true, 0>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+    }
+    if (mode == 1) return launch_t<false, 1>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+    if (mode == 2) return launch_t<false, 2>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+    return launch_t<false, 0>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
 }
 
 }  // namespace if4

@@ -20,7 +20,7 @@ MODE_ADAPTIVE, MODE_FORCE_FP4, MODE_FORCE_INT4 = 0, 1, 2
 GROUP = 16
 
 EXPORTS = ("if4_version", "if4_status_string", "if4_quantize", "if4_quantize_mode",
-           "if4_dequantize", "if4_gemm")
+           "if4_quantize_t", "if4_dequantize", "if4_gemm")
 
 
 class IF4Error(RuntimeError):
@@ -44,6 +44,8 @@ def _load():
     L.if4_quantize.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, vp]
     L.if4_quantize_mode.restype = ci
     L.if4_quantize_mode.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
+    L.if4_quantize_t.restype = ci
+    L.if4_quantize_t.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
     L.if4_dequantize.restype = ci
     L.if4_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, ci, i64, vp]
     L.if4_gemm.restype = ci
@@ -95,6 +97,25 @@ def quantize(x: torch.Tensor, scale_exp: int = 0, mode: int = MODE_ADAPTIVE, out
                                codes.data_ptr(), scales.data_ptr(), int(scale_exp), int(mode),
                                _stream(x.device))
     _check("if4_quantize_mode", st)
+    return codes, scales
+
+
+def quantize_t(x: torch.Tensor, scale_exp: int = 0, mode: int = MODE_ADAPTIVE, out=None):
+    """IF4 of x^T for a 2-D [rows, cols] CUDA tensor (unit stride along dim
+    1): groups of 16 consecutive rows of each column.  Returns (codes uint8
+    [cols, rows/2], scales uint8 [cols, rows/16])."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor with unit stride along dim 1")
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty((cols, rows // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((cols, rows // GROUP), dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    st = lib.if4_quantize_t(x.data_ptr(), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                            codes.data_ptr(), scales.data_ptr(), int(scale_exp), int(mode),
+                            _stream(x.device))
+    _check("if4_quantize_t", st)
     return codes, scales
 
 

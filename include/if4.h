@@ -101,6 +101,25 @@ int if4_quantize_mode(const void* x, int x_dtype, int64_t rows, int64_t cols,
                       int32_t scale_exp, int mode, void* stream);
 
 /*
+ * Quantize x^T: the groups are 16 consecutive ROWS of each column of x, and
+ * the result is bit for bit if4_quantize_mode applied to the transpose of x
+ * (same rules, same mode).  This is the operand layout the backward products
+ * of a W4A4G4 linear layer need, which contract over the other dimension
+ * ("Adaptive Block-Scaled Data Types", shd-paper.top card, training setup:
+ * weights, activations and gradients all in 4 bits): dgrad groups W along
+ * N, wgrad groups dY and X along M.
+ *   x       device [rows, cols] row-major, fp32 or bf16, aligned to its
+ *           element size, leading dimension ld_x >= cols
+ *   rows    multiple of 16 (else IF4_ERR_SHAPE); cols any
+ *   codes   device [cols, rows/2], 8-byte aligned (row c = column c of x)
+ *   scales  device [cols, rows/16]
+ * Errors as if4_quantize.
+ */
+int if4_quantize_t(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                   int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                   int32_t scale_exp, int mode, void* stream);
+
+/*
  * Dequantize IF4 to fp32 or bf16.  INT4 magnitudes are descaled by 6/7
  * (gist.science summary, section 2, "Metodo 6/7"):
  *   FP4   y = (+-) c * s' * 2^E             (exact in fp32)
@@ -121,9 +140,12 @@ int if4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
  * group decoded by its own scale's sign bit):
  *   C[m, n] = sum_k A[m, k] * W[n, k]       (C = A W^T, nn.Linear layout)
  * with A [M, K] and W [N, K] both IF4 grouped along K.  Each operand is
- * decoded to fp16 without its 2^E (FP4 values exactly, INT4 values
- * fl16(6 q s'/7)), products are accumulated in fp32 on the matrix cores,
- * and C is scaled by 2^(a_exp + w_exp) before the fp32 store.
+ * decoded to fp16 without its 2^E and with a uniform 2^-9: FP4 values
+ * c s' 2^-9 exactly, INT4 values fl16(|q| sigma 2^-9) with
+ * sigma = fl16(fl32(s' * fl32(6/7))), the fp16 rounding of |q| sigma
+ * (below 2^-5 to a multiple of 2^-15).  Products are accumulated in fp32 on
+ * the matrix cores and C is scaled by 2^(a_exp + w_exp + 18) before the
+ * fp32 store.
  *   a_codes [M, K/2], w_codes [N, K/2]: device, 8-byte aligned
  *   a_scales [M, K/16], w_scales [N, K/16]: device
  *   c       device fp32 [M, N] with leading dimension ldc >= N, 4-byte aligned

@@ -29,7 +29,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert names == sorted(["if4_version", "if4_status_string", "if4_quantize",
-                            "if4_quantize_mode", "if4_dequantize", "if4_gemm"])
+                            "if4_quantize_mode", "if4_quantize_t", "if4_dequantize", "if4_gemm"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -62,6 +62,25 @@ def test_quantize_validation(L):
     # empty inputs are valid and launch nothing
     assert q(L, rows=0) == 0 and q(L, rows=3, cols=0, ld=0) == 0
     assert L.if4_quantize(FAKE, 1, 0, 32, 32, FAKE, FAKE, 0, None) == 0
+
+
+def qt(L, x=FAKE, dt=1, rows=32, cols=8, ld=8, codes=FAKE, scales=FAKE, e=0, mode=0):
+    return L.if4_quantize_t(x, dt, rows, cols, ld, codes, scales, e, mode, None)
+
+
+def test_quantize_t_validation(L):
+    # every call below has exactly one bad argument, so none launches
+    assert qt(L, dt=7) == 4
+    assert qt(L, mode=3) == 4
+    assert qt(L, rows=20) == 2         # groups run down the rows
+    assert qt(L, rows=-16) == 2
+    assert qt(L, ld=4) == 2
+    assert qt(L, e=65) == 5
+    assert qt(L, x=None) == 1 and qt(L, codes=None) == 1 and qt(L, scales=None) == 1
+    assert qt(L, x=FAKE + 1, dt=1) == 3  # bf16 needs 2-byte alignment
+    assert qt(L, x=FAKE + 2, dt=0) == 3  # fp32 needs 4-byte alignment
+    assert qt(L, codes=FAKE + 4) == 3
+    assert qt(L, rows=0) == 0 and qt(L, cols=0, ld=0) == 0
 
 
 def test_dequantize_validation(L):
