@@ -322,3 +322,76 @@ void if4o_gemm_sample_f64(const uint8_t* a_codes, const uint8_t* a_scales,
     free(ad);
     free(wd);
 }
+
+/* ------------------------------------------------------------------------
+ * Random-sign 16-point Hadamard rotation before quantization.  The pages
+ * apply a Hadamard transform to smooth outliers, which makes groups more
+ * uniform and favours INT4 ([gist] section 1 "O Problema"; [podcast] "Where
+ * the Gain Actually Comes From", the Hadamard-transformed weight gradient).
+ * They give neither its size nor its arithmetic.  Reading used here: per
+ * group of 16, y = H16 (d .* x) / 4 with d the +-1 vector of sign_mask (bit i
+ * set: element i negated) and H16 the Sylvester matrix H2 (x) H2 (x) H2 (x) H2,
+ * so H16/4 is orthonormal.  In fp32 the product is taken through the butterfly
+ * stages of that Kronecker factorisation, strides 1, 2, 4, 8 in that order,
+ * each pair (lo, hi) becoming (lo + hi, lo - hi); the quarter is applied last.
+ * The rotated tensor keeps its input's precision: for bf16 input each y is
+ * rounded to bf16 (nearest even) before it is quantized, which is what the
+ * unfused rotate-then-quantize pipeline on a bf16 tensor would produce. */
+static float round_bf16(float v) {
+    uint16_t h;
+    if4o_f32_to_bf16(&v, 1, &h);
+    uint32_t u = (uint32_t)h << 16;
+    float r;
+    memcpy(&r, &u, 4);
+    return r;
+}
+
+static void rht16_group(const float* x, uint32_t sign_mask, int round_to_bf16, float y[16]) {
+    float v[GROUP];
+    for (int i = 0; i < GROUP; i++)
+        v[i] = ((sign_mask >> i) & 1u) ? -x[i] : x[i];
+    for (int h = 1; h < GROUP; h *= 2) {
+        for (int i = 0; i < GROUP; i++) {
+            if (i & h) continue;
+            float lo = v[i], hi = v[i + h];
+            v[i] = lo + hi;
+            v[i + h] = lo - hi;
+        }
+    }
+    for (int i = 0; i < GROUP; i++) {
+        float t = v[i] * 0.25f;
+        y[i] = round_to_bf16 ? round_bf16(t) : t;
+    }
+}
+
+void if4o_rht16(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                uint32_t sign_mask, int round_to_bf16, float* y, int64_t ld_y,
+                int nthreads) {
+    int64_t gpr = cols / GROUP;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t g = 0; g < gpr; g++)
+            rht16_group(x + r * ld_x + g * GROUP, sign_mask, round_to_bf16,
+                        y + r * ld_y + g * GROUP);
+}
+
+void if4o_quantize_rht(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint32_t sign_mask, int round_to_bf16, int32_t scale_exp,
+                       int mode, uint8_t* codes, uint8_t* scales, int nthreads) {
+    int64_t gpr = cols / GROUP;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t g = 0; g < gpr; g++) {
+            float y[GROUP], ef, ei;
+            rht16_group(x + r * ld_x + g * GROUP, sign_mask, round_to_bf16, y);
+            if4o_quantize_group(y, scale_exp, mode, codes + r * (cols / 2) + g * 8,
+                                scales + r * gpr + g, &ef, &ei);
+        }
+    }
+}

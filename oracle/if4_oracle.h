@@ -8,15 +8,18 @@
  *
  * Source pages (cited by title and section throughout):
  *   [gist]    "Adaptive Block-Scaled Data Types", gist.science structured
- *             summary (Portuguese): section 2 "Metodologia" with the items
- *             "Mecanismo de Selecao", "Codificacao Eficiente", "Metodo 6/7".
+ *             summary (Portuguese): section 1 "O Problema" (Hadamard
+ *             transforms make data uniform); section 2 "Metodologia" with the
+ *             items "Mecanismo de Selecao", "Codificacao Eficiente",
+ *             "Metodo 6/7".
  *   [card]    "Adaptive Block-Scaled Data Types", shd-paper.top paper card:
  *             "方法详解" (method details) -- technical framework steps 1-5,
  *             key design; and the English abstract.
  *   [podcast] "Adaptive Block-Scaled Data Types for FP4 Training", episode
  *             companion: "One Group, Two Candidate Encodings", "The Free Bit:
  *             Scale Factor Sign", "MAC Unit: Decoding Two Formats from One
- *             Sign Bit".
+ *             Sign Bit", "Where the Gain Actually Comes From" (the
+ *             Hadamard-transformed weight gradient).
  *   [fugumt]  "論文の概要: Adaptive Block-Scaled Data Types": related-paper
  *             entry "FP8 Formats for Deep Learning" (E4M3 has no infinities
  *             and a single NaN mantissa pattern).
@@ -25,8 +28,9 @@
  * notes; each is restated next to the code that implements it.
  *
  * Pins: every function here is checked by the CPU tests against closed forms,
- * exhaustive brute force and an exact-rational re-implementation; see
- * tests/test_oracle_pins.py.
+ * exhaustive brute force and an exact-rational re-implementation (see
+ * tests/test_oracle_pins.py); the Hadamard rotation against scipy's Sylvester
+ * matrix, its error bound and hand-worked fp32 groups (tests/test_oracle_rht.py).
  */
 #ifndef IF4_ORACLE_H
 #define IF4_ORACLE_H
@@ -95,6 +99,19 @@ void if4o_gemm_sample_f64(const uint8_t* a_codes, const uint8_t* a_scales,
                           const int64_t* row_idx, int64_t n_rows,
                           const int64_t* col_idx, int64_t n_cols, double* c,
                           int nthreads);
+
+/* Random-sign Hadamard rotation of each group of 16 along dim 1:
+ * y = H16 (d .* x) / 4, d_i = -1 where bit i of sign_mask is set, computed in
+ * fp32 butterflies of strides 1, 2, 4, 8 (see the .c file for the reading);
+ * with round_to_bf16 each y is rounded to bf16 (kept as fp32). */
+void if4o_rht16(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                uint32_t sign_mask, int round_to_bf16, float* y, int64_t ld_y,
+                int nthreads);
+
+/* IF4 of the rotated tensor: if4o_rht16 followed by if4o_quantize. */
+void if4o_quantize_rht(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint32_t sign_mask, int round_to_bf16, int32_t scale_exp,
+                       int mode, uint8_t* codes, uint8_t* scales, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -52,6 +52,12 @@ def lib():
         L.if4o_gemm_sample_f64.argtypes = [c_u8p, c_u8p, i32, c_u8p, c_u8p, i32, i64,
                                            c_i64p, i64, c_i64p, i64, c_f64p,
                                            ctypes.c_int]
+        L.if4o_rht16.restype = None
+        L.if4o_rht16.argtypes = [c_f32p, i64, i64, i64, ctypes.c_uint32, ctypes.c_int, c_f32p,
+                                 i64, ctypes.c_int]
+        L.if4o_quantize_rht.restype = None
+        L.if4o_quantize_rht.argtypes = [c_f32p, i64, i64, i64, ctypes.c_uint32, ctypes.c_int,
+                                        i32, ctypes.c_int, c_u8p, c_u8p, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -153,3 +159,30 @@ def gemm_sample_f64(a_codes, a_scales, a_exp, w_codes, w_scales, w_exp, rows=Non
                                _ptr(cols, ctypes.c_int64), cols.size,
                                _ptr(c, ctypes.c_double), nthreads)
     return c
+
+
+def rht16(x, sign_mask: int, round_to_bf16: bool = False, nthreads: int = 0):
+    """Per-group random-sign Hadamard rotation along dim 1 (fp32 butterflies;
+    bit i of sign_mask negates element i of every group).  Returns fp32
+    [rows, cols]; with round_to_bf16 every value is bf16-exact."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    assert cols % GROUP == 0
+    y = np.zeros((rows, cols), np.float32)
+    lib().if4o_rht16(_ptr(x, ctypes.c_float), rows, cols, cols, sign_mask & 0xFFFF,
+                     int(round_to_bf16), _ptr(y, ctypes.c_float), cols, nthreads)
+    return y
+
+
+def quantize_rht(x, sign_mask: int, scale_exp: int = 0, mode: int = ADAPTIVE,
+                 round_to_bf16: bool = False, nthreads: int = 0):
+    """IF4 of rht16(x, sign_mask, round_to_bf16): (codes, scales)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    assert cols % GROUP == 0
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // GROUP), np.uint8)
+    lib().if4o_quantize_rht(_ptr(x, ctypes.c_float), rows, cols, cols, sign_mask & 0xFFFF,
+                            int(round_to_bf16), scale_exp, mode, _ptr(codes, ctypes.c_uint8),
+                            _ptr(scales, ctypes.c_uint8), nthreads)
+    return codes, scales
