@@ -72,6 +72,17 @@ int if4_quantize_mode(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                            scales, scale_exp, mode, (hipStream_t)stream));
 }
 
+int if4_quantize_rht(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                     int64_t ld_x, uint32_t sign_mask, uint8_t* codes, uint8_t* scales,
+                     int32_t scale_exp, int mode, void* stream) {
+    if (sign_mask > 0xFFFFu) return IF4_ERR_RANGE;
+    int st = check_quantize(x, x_dtype, rows, cols, ld_x, codes, scales, scale_exp, mode);
+    if (st != IF4_OK || rows == 0 || cols == 0) return st;
+    return hip_status(if4::launch_quantize_rht(x, x_dtype == IF4_BF16, rows, cols, ld_x,
+                                               sign_mask, codes, scales, scale_exp, mode,
+                                               (hipStream_t)stream));
+}
+
 int if4_quantize_t(const void* x, int x_dtype, int64_t rows, int64_t cols,
                    int64_t ld_x, uint8_t* codes, uint8_t* scales,
                    int32_t scale_exp, int mode, void* stream) {

@@ -21,6 +21,11 @@ hipError_t launch_quantize(const void* x, int bf16, int64_t rows, int64_t cols,
                            int64_t ld_x, uint8_t* codes, uint8_t* scales,
                            int32_t scale_exp, int mode, hipStream_t stream);
 
+hipError_t launch_quantize_rht(const void* x, int bf16, int64_t rows, int64_t cols,
+                               int64_t ld_x, uint32_t sign_mask, uint8_t* codes,
+                               uint8_t* scales, int32_t scale_exp, int mode,
+                               hipStream_t stream);
+
 hipError_t launch_quantize_t(const void* x, int bf16, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t* codes, uint8_t* scales,
                              int32_t scale_exp, int mode, hipStream_t stream);

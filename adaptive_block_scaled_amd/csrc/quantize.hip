@@ -152,13 +152,38 @@ __device__ __forceinline__ void exact_group(const float (&v)[16], float p_exp, f
     }
 }
 
+// Random-sign 16-point Hadamard rotation applied before quantization: the
+// pages use a Hadamard transform to smooth outliers, which leaves groups more
+// uniform and favours the INT4 encoding ("Adaptive Block-Scaled Data Types",
+// gist.science summary, section 1 "O Problema"; podcast companion, "Where the
+// Gain Actually Comes From").  Per group y = H16 (d .* x) / 4 with H16 the
+// Sylvester matrix H2 (x) H2 (x) H2 (x) H2, taken in fp32 through its butterfly
+// stages, strides 1, 2, 4, 8 in that order, each pair (lo, hi) becoming
+// (lo + hi, lo - hi), then the exact quarter.  The caller has already applied
+// the signs d (an xor of the input's sign bits, exact).
+__device__ __forceinline__ void hadamard16(float (&v)[16]) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            if (i & h) continue;
+            const float lo = v[i], hi = v[i + h];
+            v[i] = lo + hi;
+            v[i + h] = lo - hi;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] *= 0.25f;
+}
+
 // ---------------------------------------------------------------------------
 // Exact reference path (any fp32 input): thresholds compared exactly.
-template <bool kBf16, int kMode>
+template <bool kBf16, int kMode, bool kRotate>
 __global__ void __launch_bounds__(kThreads)
 quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
-                      float p_negexp) {
+                      float p_negexp, uint32_t sign_mask) {
     const int64_t ngroups = rows * gpr;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < ngroups; g += stride) {
@@ -166,6 +191,16 @@ quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int
         const int64_t cg = g - r * gpr;
         float v[16];
         load_group<kBf16>(x, r * ld_x + cg * 16, v);
+        if constexpr (kRotate) {
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+            hadamard16(v);
+            if constexpr (kBf16) {  // the rotated tensor keeps bf16 precision
+#pragma unroll
+                for (int i = 0; i < 16; i++) v[i] = (float)(__bf16)v[i];
+            }
+        }
 
         uint32_t lo, hi, byte;
         exact_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
@@ -318,14 +353,20 @@ __device__ __forceinline__ void fast_group(const float (&v)[16], const float2* r
     }
 }
 
-template <int kMode, bool kContig>
+template <int kMode, bool kContig, bool kRotate>
 __global__ void __launch_bounds__(kThreads)
 quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
-                     float p_negexp) {
+                     float p_negexp, uint32_t sign_mask) {
     __shared__ float2 recip[128];
     fill_recip(recip);
     __syncthreads();
+    // sign-bit xor words for the rotation: bf16 element 2j sits in the low
+    // half of input word j, element 2j + 1 in the high half
+    uint32_t flip[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        flip[j] = (((sign_mask >> (2 * j)) & 1u) << 15) | (((sign_mask >> (2 * j + 1)) & 1u) << 31);
 
     const int64_t ngroups = rows * gpr;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -340,12 +381,23 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
         return reinterpret_cast<const uint4*>(x + off);
     };
     auto quantize_group = [&](const uint4 va, const uint4 vb, const int64_t g) {
-        const uint32_t w[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        uint32_t w[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        if constexpr (kRotate) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) w[i] ^= flip[i];
+        }
         float v[16];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             v[2 * i] = __uint_as_float(w[i] << 16);
             v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        if constexpr (kRotate) {
+            // rotate in fp32, then round back to bf16 (nearest even): the
+            // values the fast path below needs are bf16-exact
+            hadamard16(v);
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = (float)(__bf16)v[i];
         }
         uint32_t lo, hi, byte;
         fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
@@ -385,9 +437,9 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
 #define IF4_QUANT_BLOCKS 8192
 #endif
 
-template <bool kBf16, int kMode>
+template <bool kBf16, int kMode, bool kRotate>
 hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
-                  uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
+                  uint8_t* scales, int32_t scale_exp, uint32_t sign_mask, hipStream_t stream) {
     const int64_t gpr = cols / 16;
     const int64_t ngroups = rows * gpr;
     int64_t blocks = (ngroups + kThreads - 1) / kThreads;
@@ -399,14 +451,17 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
     if constexpr (kBf16) {
         const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
         if (ld_x == cols)
-            hipLaunchKernelGGL((quantize_bf16_kernel<kMode, true>), dim3((unsigned)blocks),
-                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales, pe, pn);
+            hipLaunchKernelGGL((quantize_bf16_kernel<kMode, true, kRotate>),
+                               dim3((unsigned)blocks), dim3(kThreads), 0, stream, xb, rows, gpr,
+                               ld_x, codes, scales, pe, pn, sign_mask);
         else
-            hipLaunchKernelGGL((quantize_bf16_kernel<kMode, false>), dim3((unsigned)blocks),
-                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales, pe, pn);
+            hipLaunchKernelGGL((quantize_bf16_kernel<kMode, false, kRotate>),
+                               dim3((unsigned)blocks), dim3(kThreads), 0, stream, xb, rows, gpr,
+                               ld_x, codes, scales, pe, pn, sign_mask);
     } else {
-        hipLaunchKernelGGL((quantize_exact_kernel<false, kMode>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales, pe, pn);
+        hipLaunchKernelGGL((quantize_exact_kernel<false, kMode, kRotate>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales, pe, pn,
+                           sign_mask);
     }
     return hipGetLastError();
 }
@@ -481,24 +536,38 @@ hipError_t launch_t(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uin
     return hipGetLastError();
 }
 
+template <bool kRotate>
+hipError_t dispatch_quantize(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t* codes, uint8_t* scales, int32_t scale_exp, int mode,
+                             uint32_t sign_mask, hipStream_t stream) {
+#define IF4_Q(B, M) \
+    launch<B, M, kRotate>(x, rows, cols, ld_x, codes, scales, scale_exp, sign_mask, stream)
+    if (bf16) {
+        if (mode == 1) return IF4_Q(true, 1);
+        if (mode == 2) return IF4_Q(true, 2);
+        return IF4_Q(true, 0);
+    }
+    if (mode == 1) return IF4_Q(false, 1);
+    if (mode == 2) return IF4_Q(false, 2);
+    return IF4_Q(false, 0);
+#undef IF4_Q
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ld_x,
                            uint8_t* codes, uint8_t* scales, int32_t scale_exp, int mode,
                            hipStream_t stream) {
-    if (bf16) {
-        if (mode == 1) return launch<true, 1>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
-        if (mode == 2) return launch<true, 2>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
-        return launch<true, 0>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
-    }
-    if (mode == 1) return launch<false, 1>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
-    if (mode == 2) return launch<false, 2>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
-    return launch<false, 0>(x, rows, cols, ld_x, codes, scales, scale_exp, stream);
+    return dispatch_quantize<false>(x, bf16, rows, cols, ld_x, codes, scales, scale_exp, mode, 0u,
+                                    stream);
 }
 
-}  // namespace if4
-
-namespace if4 {
+hipError_t launch_quantize_rht(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                               uint32_t sign_mask, uint8_t* codes, uint8_t* scales,
+                               int32_t scale_exp, int mode, hipStream_t stream) {
+    return dispatch_quantize<true>(x, bf16, rows, cols, ld_x, codes, scales, scale_exp, mode,
+                                   sign_mask, stream);
+}
 
 hipError_t launch_quantize_t(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t* codes, uint8_t* scales, int32_t scale_exp, int mode,

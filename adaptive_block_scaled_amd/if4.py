@@ -20,7 +20,7 @@ MODE_ADAPTIVE, MODE_FORCE_FP4, MODE_FORCE_INT4 = 0, 1, 2
 GROUP = 16
 
 EXPORTS = ("if4_version", "if4_status_string", "if4_quantize", "if4_quantize_mode",
-           "if4_quantize_t", "if4_dequantize", "if4_gemm")
+           "if4_quantize_t", "if4_quantize_rht", "if4_dequantize", "if4_gemm")
 
 
 class IF4Error(RuntimeError):
@@ -46,6 +46,8 @@ def _load():
     L.if4_quantize_mode.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
     L.if4_quantize_t.restype = ci
     L.if4_quantize_t.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
+    L.if4_quantize_rht.restype = ci
+    L.if4_quantize_rht.argtypes = [vp, ci, i64, i64, i64, ctypes.c_uint32, vp, vp, i32, ci, vp]
     L.if4_dequantize.restype = ci
     L.if4_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, ci, i64, vp]
     L.if4_gemm.restype = ci
@@ -116,6 +118,27 @@ def quantize_t(x: torch.Tensor, scale_exp: int = 0, mode: int = MODE_ADAPTIVE, o
                             codes.data_ptr(), scales.data_ptr(), int(scale_exp), int(mode),
                             _stream(x.device))
     _check("if4_quantize_t", st)
+    return codes, scales
+
+
+def quantize_rht(x: torch.Tensor, sign_mask: int, scale_exp: int = 0, mode: int = MODE_ADAPTIVE,
+                 out=None):
+    """IF4 of x after a random-sign 16-point Hadamard rotation of every group
+    along dim 1 (bit i of sign_mask negates element i of each group first).
+    Same layout and return as quantize(); the rotated values never reach
+    memory."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor with unit stride along dim 1")
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // GROUP), dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    st = lib.if4_quantize_rht(x.data_ptr(), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                              int(sign_mask), codes.data_ptr(), scales.data_ptr(),
+                              int(scale_exp), int(mode), _stream(x.device))
+    _check("if4_quantize_rht", st)
     return codes, scales
 
 

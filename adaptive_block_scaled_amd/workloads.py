@@ -130,6 +130,21 @@ def c3_rht_gradient(seed: int = 0, rows: int = 16384, cols: int = 4096) -> Tenso
                   to_bf16_f32(rht_gradient(rows, cols, seed)), "bf16")
 
 
+def sign_mask(d: np.ndarray) -> int:
+    """16-bit mask of a +-1 vector: bit i set where d_i = -1."""
+    return int(sum(1 << i for i in range(GROUP) if d[i] < 0))
+
+
+def c3_raw_gradient(seed: int = 0, rows: int = 16384, cols: int = 4096):
+    """The gradient before its rotation, as a bf16 tensor, and the rotation's
+    sign mask: the input of the fused rotate-and-quantize.  Same draws, in the
+    same order, as rht_gradient (values first, then the 16 signs)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(1e-3)
+    d = random_signs(rng)
+    return Tensor(f"c3_raw_grad_bf16_{rows}x{cols}", to_bf16_f32(x), "bf16"), sign_mask(d)
+
+
 def c4_gemm(seed: int = 0, m: int = 4096, n: int = 4096, k: int = 4096):
     a = Tensor(f"c4_A_bf16_{m}x{k}", to_bf16_f32(outlier_activations(m, k, seed)), "bf16")
     w = Tensor(f"c4_W_bf16_{n}x{k}", to_bf16_f32(normal_weights(n, k, seed + 1)), "bf16")

@@ -101,6 +101,31 @@ int if4_quantize_mode(const void* x, int x_dtype, int64_t rows, int64_t cols,
                       int32_t scale_exp, int mode, void* stream);
 
 /*
+ * Rotate, then quantize: each group of 16 along dim 1 is first turned by a
+ * random-sign 16-point Hadamard transform, the preprocessing the pages use to
+ * smooth outliers so that groups look uniform and the INT4 encoding wins more
+ * often ("Adaptive Block-Scaled Data Types", gist.science summary, section 1
+ * "O Problema"; podcast companion, "Where the Gain Actually Comes From").
+ * Per group, y = H16 (d .* x) / 4, with d_i = -1 where bit i of sign_mask is
+ * set and H16 the Sylvester matrix H2 (x) H2 (x) H2 (x) H2 (orthonormal after
+ * the 1/4).  Arithmetic: fp32, through the butterfly stages of that
+ * factorisation, strides 1, 2, 4, 8 in that order, each pair (lo, hi) ->
+ * (lo + hi, lo - hi) rounded to nearest even, then the exact quarter; for
+ * bf16 input each y is rounded to bf16 (nearest even) before it is
+ * quantized.  The result is bit for bit if4_quantize_mode of that rotated
+ * tensor, with y never written to memory.  The same sign_mask applied to both
+ * operands of a product along their contraction dim leaves the product
+ * unchanged (H16/4 is orthogonal), so a GEMM of two rotated operands
+ * approximates the unrotated one.
+ *   sign_mask  bits 0..15 (higher bits set: IF4_ERR_RANGE)
+ * Other arguments, alignment and errors as if4_quantize_mode.  scale_exp
+ * refers to the rotated values, whose absmax is at most 4x that of x.
+ */
+int if4_quantize_rht(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                     int64_t ld_x, uint32_t sign_mask, uint8_t* codes,
+                     uint8_t* scales, int32_t scale_exp, int mode, void* stream);
+
+/*
  * Quantize x^T: the groups are 16 consecutive ROWS of each column of x, and
  * the result is bit for bit if4_quantize_mode applied to the transpose of x
  * (same rules, same mode).  This is the operand layout the backward products

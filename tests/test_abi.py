@@ -29,7 +29,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert names == sorted(["if4_version", "if4_status_string", "if4_quantize",
-                            "if4_quantize_mode", "if4_quantize_t", "if4_dequantize", "if4_gemm"])
+                            "if4_quantize_mode", "if4_quantize_t", "if4_quantize_rht",
+                            "if4_dequantize", "if4_gemm"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -81,6 +82,27 @@ def test_quantize_t_validation(L):
     assert qt(L, x=FAKE + 2, dt=0) == 3  # fp32 needs 4-byte alignment
     assert qt(L, codes=FAKE + 4) == 3
     assert qt(L, rows=0) == 0 and qt(L, cols=0, ld=0) == 0
+
+
+def qr(L, x=FAKE, dt=1, rows=4, cols=32, ld=32, mask=0x1234, codes=FAKE, scales=FAKE, e=0,
+       mode=0):
+    return L.if4_quantize_rht(x, dt, rows, cols, ld, mask, codes, scales, e, mode, None)
+
+
+def test_quantize_rht_validation(L):
+    # every call below has exactly one bad argument, so none launches
+    assert qr(L, mask=0x10000) == 5 and qr(L, mask=0xFFFFFFFF) == 5
+    assert qr(L, dt=7) == 4
+    assert qr(L, mode=3) == 4
+    assert qr(L, cols=40, ld=40) == 2  # groups run along the rows
+    assert qr(L, ld=16) == 2
+    assert qr(L, rows=-1) == 2
+    assert qr(L, e=-65) == 5
+    assert qr(L, x=None) == 1 and qr(L, codes=None) == 1 and qr(L, scales=None) == 1
+    assert qr(L, x=FAKE + 2) == 3
+    assert qr(L, ld=36) == 3           # 72-byte rows break 16-byte alignment
+    assert qr(L, codes=FAKE + 4) == 3
+    assert qr(L, rows=0) == 0 and qr(L, cols=0, ld=0) == 0
 
 
 def test_dequantize_validation(L):
