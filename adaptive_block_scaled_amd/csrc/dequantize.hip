@@ -121,25 +121,37 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
         }
     };
 
-    int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    uint2 cw = make_uint2(0, 0);
-    uint32_t b = 0;
-    if (g < ngroups) {
-        cw = *reinterpret_cast<const uint2*>(codes + g * 8);
-        b = scales[g];
-    }
-    for (; g < ngroups; g += stride) {
-        const uint2 c0 = cw;
-        const uint32_t b0 = b;
-        if (g + stride < ngroups) {
-            cw = *reinterpret_cast<const uint2*>(codes + (g + stride) * 8);
-            b = scales[g + stride];
-        }
-        const Entry e = table[b0];
+    // Grid-stride loop over pairs of groups; the next group's codes and scale
+    // byte are loaded into the other of two register sets while the current
+    // group is decoded.  Nothing in the loop body branches: past the end of
+    // the tensor the second group of a pair is the last group again (loaded,
+    // decoded and stored a second time, with identical bytes).  A load behind
+    // a branch, or one whose value some path does not use, makes the compiler
+    // wait for it early or sink it below the current group's work, and the
+    // prefetch would hide nothing.
+    const int64_t last = ngroups - 1;
+    auto load = [&](int64_t gg, uint2& cw, uint32_t& b) {
+        cw = *reinterpret_cast<const uint2*>(codes + gg * 8);
+        b = scales[gg];
+    };
+    auto decode_store = [&](const uint2 cw, const uint32_t b, int64_t gg) {
+        const Entry e = table[b];
         float out[16];
-        decode_word(c0.x, e, out);
-        decode_word(c0.y, e, out + 8);
-        store(g, out);
+        decode_word(cw.x, e, out);
+        decode_word(cw.y, e, out + 8);
+        store(gg, out);
+    };
+    int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint2 c0, c1;
+    uint32_t b0, b1;
+    load(g < last ? g : last, c0, b0);
+    for (; g < ngroups; g += 2 * stride) {
+        const int64_t g1 = g + stride < last ? g + stride : last;
+        load(g1, c1, b1);
+        decode_store(c0, b0, g);
+        const int64_t g2 = g + 2 * stride < last ? g + 2 * stride : last;
+        load(g2, c0, b0);
+        decode_store(c1, b1, g1);
     }
 }
 

@@ -407,7 +407,10 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
 
     // Each thread walks its groups with a stride of the whole grid (a few
     // waves per SIMD); the next group's 32 input bytes are loaded while the
-    // current one is quantized, into the other of two register sets.
+    // current one is quantized, into the other of two register sets.  (A
+    // branch-free form of this loop, with clamped unconditional loads, lets
+    // the compiler keep more loads in flight; it measured 7-9% slower on
+    // tensors larger than the last-level cache, though faster on ones that fit.)
     int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint4 a0 = make_uint4(0, 0, 0, 0), b0 = a0, a1 = a0, b1 = a0;
     if (g < ngroups) {
