@@ -234,14 +234,19 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
 // codes of slab s+2 into the register set that slab s used; scales arrive a
 // window ahead.  The slab loop is unrolled by the 4-slab window so that all
 // register sets are fixed and no loaded value is copied (a copy would wait
-// for its load).  One LDS-only barrier per slab.  Within a slab, each
-// MFMA step runs A block 0 against W blocks 0..7, then A block 1, in four
-// sub-blocks of four MFMAs; each sub-block carries one code-word decode
-// (about 16 VALU instructions) and the W fragment reads of the next step.
-// A block 0's operand of step t is replaced in sub-block 2 of step t, A
-// block 1's in sub-block 0 of step t+1 -- for the last step that is step 0
-// of the next slab, from a word kept across the barrier.  Rows past M or N
-// load their nearest in-range row (those outputs are never stored).
+// for its load).  One LDS-only barrier per slab, after which the eight W
+// fragments of the slab's first step are read before any MFMA is issued.
+// Within a slab, each MFMA step runs four sub-blocks of four MFMAs: (A block
+// 0, W blocks 0..3), (1, 0..3), (0, 4..7), (1, 4..7), so that each W
+// fragment's next-step read is issued two sub-blocks before its next use.
+// Each sub-block carries one code-word decode (about 16 VALU instructions):
+// A block 1's operand of step t-1 in sub-block 0 (for step 0, from a word
+// kept across the barrier), W words in sub-blocks 1 and 2, A block 0's
+// operand of step t in sub-block 3.  The scale-table lookups of a step's
+// decodes are issued at the start of the step before (LDS operations
+// complete in order, so a lookup issued after the fragment reads would make
+// its consumer wait for them too).  Rows past M or N load their nearest
+// in-range row (those outputs are never stored).
 template <bool kWide>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -349,6 +354,12 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     half8 a[2][kGroups];   // decoded A operands [block][MFMA step] of the running slab
     uint32_t w13;          // A block 1, last step: word and scale of the running slab
     GroupScale s13;
+    // Scale-table lookups run one MFMA step ahead of the decodes that use
+    // them: issued before that step's fragment prefetches, a lookup can be
+    // waited for (LDS operations complete in order) without waiting for the
+    // prefetches too.  la1 / la0 / lw: A block 1 (previous step's word),
+    // A block 0 and W of the coming step.
+    GroupScale la1, la0, lw;
 
     // prologue: slab 0 decoded (W into buffer 0, A into registers), slab 1 fetched
     if constexpr (kWide) {
@@ -369,6 +380,10 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     }
     w13 = raw[0].aword(1, kGroups - 1);
     s13 = a_scale(raw[0], win[0], 0, 0, 1, kGroups - 1);
+    // lookups for step 0 of slab 0, which decodes slab 1
+    la1 = s13;
+    la0 = a_scale(raw[1], win[0], 1, 1, 0, 0);
+    lw = w_scale(raw[1], win[0], 1, 1, 0, 0);
     lds_barrier();
 
     const int w_off = lane * 16;  // fragment (block j, step t) at j * FRAG_BLOCK + t * FRAG_STEP
@@ -386,26 +401,46 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         // slab s+2, clamped: past the end the loads repeat the last slab and
         // the decodes fill registers and a buffer that nobody reads again
         const int64_t sl = (int64_t)s + 2 < last ? (int64_t)s + 2 : last;
-        raw[P].load(acp, asp, wcp, wsp, sl, h, q, gpr);
-        // scales of slab s+1: slot U+1 of this window, or slot 0 of the next
+        // scales of slab s+1: slot U+1 of this window, or slot 0 of the next;
+        // of slab s+2 (looked up in the last step): slot U+2 of either
         const WinScales& sw_win = U + 1 < kWin ? wcur : wnxt;
         constexpr int US = (U + 1) % kWin;
+        const WinScales& sw2_win = U + 2 < kWin ? wcur : wnxt;
+        constexpr int US2 = (U + 2) % kWin;
         const SlabCodes<kWide>& x = raw[Q];
 
+        // step 0's fragments first, all eight before any MFMA, so that only
+        // the first read's latency is exposed after the barrier
         half8 bv[8];
 #pragma unroll
         for (int j = 0; j < 8; j++)
             bv[j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
+        __builtin_amdgcn_sched_barrier(0);
+        raw[P].load(acp, asp, wcp, wsp, sl, h, q, gpr);
 #pragma unroll
         for (int t = 0; t < kGroups; t++) {
             const int k = t >> 1, gg = t & 1;
-            const GroupScale sw = w_scale(x, sw_win, US, sn, k, gg);
+            const GroupScale sa1 = la1, sa0 = la0, sw = lw;
+            if (t + 1 < kGroups) {
+                la1 = a_scale(x, sw_win, US, sn, 1, t);
+                la0 = a_scale(x, sw_win, US, sn, 0, t + 1);
+                lw = w_scale(x, sw_win, US, sn, (t + 1) >> 1, (t + 1) & 1);
+            } else {
+                // step 0 of the next slab: A block 1's last word of slab s+1,
+                // then A block 0 and W of slab s+2
+                la1 = a_scale(x, sw_win, US, sn, 1, kGroups - 1);
+                la0 = a_scale(raw[P], sw2_win, US2, sn + 1, 0, 0);
+                lw = w_scale(raw[P], sw2_win, US2, sn + 1, 0, 0);
+            }
+            // sub-blocks: (A block 0, W 0..3), (1, 0..3), (0, 4..7), (1, 4..7):
+            // W fragments 0..3 are free after sub-block 1 and 4..7 after 3,
+            // two sub-blocks before the next step needs them
 #pragma unroll
             for (int sb = 0; sb < 4; sb++) {
-                const int i = sb >> 1;  // A block of this sub-block's MFMAs
+                const int i = sb & 1;  // A block of this sub-block's MFMAs
 #pragma unroll
                 for (int jj = 0; jj < 4; jj++) {
-                    const int j = 4 * (sb & 1) + jj;
+                    const int j = 4 * (sb >> 1) + jj;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][t], bv[j], acc[i][j],
                                                                        0, 0, 0);
                     // last use of fragment j in this step: fetch the next step's
@@ -414,16 +449,17 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                                                                 (t + 1) * FRAG_STEP);
                 }
                 if (sb == 0) {
-                    if (t == 0)
-                        a[1][kGroups - 1] = decode_half(w13, s13);
-                    else
-                        a[1][t - 1] = decode_half(x.aword(1, t - 1),
-                                                  a_scale(x, sw_win, US, sn, 1, t - 1));
-                } else if (sb == 2) {
-                    a[0][t] = decode_half(x.aword(0, t), a_scale(x, sw_win, US, sn, 0, t));
+                    // t = 0: the word kept from the previous slab (sa1 holds its scale)
+                    a[1][t == 0 ? kGroups - 1 : t - 1] =
+                        decode_half(t == 0 ? w13 : x.aword(1, t - 1), sa1);
+                } else if (sb == 3) {
+                    a[0][t] = decode_half(x.aword(0, t), sa0);  // its last use was sub-block 2
                 } else {
                     w_store(x, sw, k, gg, sb == 1 ? 0 : 1, nbuf);
                 }
+                // the slab's first sub-block starts with its decode (registers
+                // only), which covers the wait for the first fragment
+                if (t == 0 && sb == 0) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -436,7 +472,6 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
             }
         }
         w13 = x.aword(1, kGroups - 1);
-        s13 = a_scale(x, sw_win, US, sn, 1, kGroups - 1);
         lds_barrier();
     };
 
