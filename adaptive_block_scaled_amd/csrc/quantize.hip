@@ -527,15 +527,183 @@ quantize_t_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_
     }
 }
 
+// Tiled form of the x^T quantize, for 16-byte aligned rows: a workgroup
+// stages a tile of 128 rows x 128 columns of x in LDS with 16-byte loads (a
+// wave loads 4 rows, 256 contiguous bytes each for bf16), then each lane takes
+// a pair of adjacent columns and two consecutive row-groups (wave w: row-groups
+// 2w, 2w+1 of the tile) and reads its 32 rows as one word per row -- both
+// columns at once; the 64 lanes of a wave read one contiguous 256-byte row
+// (512 for fp32), so the reads are free of bank conflicts.  Each lane then
+// quantizes its four groups.  The results go back through the same LDS
+// (codes [128 columns][64 bytes], scales [128 columns][8 bytes]) so that the
+// workgroup writes each column's 64 code bytes and 8 scale bytes with
+// neighbouring lanes on neighbouring bytes: written straight from the lanes,
+// every store instruction touched 64 cache lines, one per column.
+constexpr int kTR = 128, kTC = 128;  // tile rows (8 row-groups) and columns
+constexpr int kTRG = kTR / 16;       // row-groups per tile
+
+template <bool kBf16, int kMode>
+__global__ void __launch_bounds__(kThreads)
+quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
+                       float p_negexp, int64_t col_tiles, int wide_out) {
+    constexpr int kElem = kBf16 ? 2 : 4;
+    constexpr int kRowBytes = kTC * kElem;        // 256 (bf16) or 512 (fp32)
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kRowBytes];
+    __shared__ float2 recip[128];
+    if constexpr (kBf16) fill_recip(recip);
+
+    const int64_t ct = blockIdx.x % col_tiles, rt = blockIdx.x / col_tiles;
+    const int64_t c0 = ct * kTC, r0 = rt * kTR;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+
+    // stage: 16-byte chunks, row-major in LDS; out-of-range rows and columns
+    // read as zero (their groups are never stored).  Interior tiles skip the
+    // checks and address with 32-bit offsets from the tile's first element.
+    constexpr int kChunksPerRow = kRowBytes / 16, kElemsPerChunk = 16 / kElem;
+    constexpr int kLoads = kTR * kChunksPerRow / kThreads;
+    if (r0 + kTR <= rows && c0 + kTC <= cols) {
+        const uint8_t* base = xb + (r0 * ld_x + c0) * kElem;
+        const uint32_t ld_bytes = (uint32_t)(ld_x * kElem);
+#pragma unroll
+        for (int i = 0; i < kLoads; i++) {
+            const int chunk = i * kThreads + tid;
+            const int rr = chunk / kChunksPerRow, cc = chunk % kChunksPerRow;
+            *reinterpret_cast<uint4*>(tile + rr * kRowBytes + cc * 16) =
+                *reinterpret_cast<const uint4*>(base + rr * ld_bytes + cc * 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kLoads; i++) {
+            const int chunk = i * kThreads + tid;
+            const int rr = chunk / kChunksPerRow, cc = chunk % kChunksPerRow;
+            const int64_t r = r0 + rr, c = c0 + (int64_t)cc * kElemsPerChunk;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (r < rows) {
+                const uint8_t* src = xb + (r * ld_x + c) * kElem;
+                if (c + kElemsPerChunk <= cols) {
+                    v = *reinterpret_cast<const uint4*>(src);
+                } else if (c < cols) {
+                    uint32_t w[4] = {0, 0, 0, 0};
+                    for (int e = 0; e < (int)(cols - c); e++) {
+                        const uint32_t val = kBf16
+                                                 ? (uint32_t)reinterpret_cast<const uint16_t*>(src)[e]
+                                                 : reinterpret_cast<const uint32_t*>(src)[e];
+                        if constexpr (kBf16)
+                            w[e >> 1] |= val << (16 * (e & 1));
+                        else
+                            w[e] = val;
+                    }
+                    v = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+            *reinterpret_cast<uint4*>(tile + rr * kRowBytes + cc * 16) = v;
+        }
+    }
+    __syncthreads();
+
+    // this lane: tile columns 2*lane, 2*lane + 1; tile row-groups 2*wave, +1
+    float ve[32], vo[32];  // the two columns, 32 rows
+#pragma unroll
+    for (int rr = 0; rr < 32; rr++) {
+        const uint8_t* p = tile + (32 * wave + rr) * kRowBytes + 2 * lane * kElem;
+        if constexpr (kBf16) {
+            const uint32_t wd = *reinterpret_cast<const uint32_t*>(p);
+            ve[rr] = __uint_as_float(wd << 16);
+            vo[rr] = __uint_as_float(wd & 0xFFFF0000u);
+        } else {
+            const uint2 wd = *reinterpret_cast<const uint2*>(p);
+            ve[rr] = __uint_as_float(wd.x);
+            vo[rr] = __uint_as_float(wd.y);
+        }
+    }
+    auto group = [&](const float* src, uint32_t& lo, uint32_t& hi, uint32_t& byte) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = src[i];
+        if constexpr (kBf16)
+            fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
+        else
+            exact_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
+    };
+    uint32_t lo[2][2], hi[2][2], by[2][2];  // [column][row-group]
+#pragma unroll
+    for (int cj = 0; cj < 2; cj++) {
+        group(cj == 0 ? ve : vo, lo[cj][0], hi[cj][0], by[cj][0]);
+        group((cj == 0 ? ve : vo) + 16, lo[cj][1], hi[cj][1], by[cj][1]);
+    }
+
+    // results into LDS (every lane has read its rows), then out column-wise
+    constexpr int kCodeRow = kTRG * 8;             // 64 code bytes per column
+    uint8_t* ocodes = tile;                        // [kTC][kCodeRow]
+    uint8_t* oscales = tile + kTC * kCodeRow;      // [kTC][kTRG]
+    __syncthreads();
+#pragma unroll
+    for (int cj = 0; cj < 2; cj++) {
+        const int lc = 2 * lane + cj;
+        *reinterpret_cast<uint4*>(ocodes + lc * kCodeRow + 2 * wave * 8) =
+            make_uint4(lo[cj][0], hi[cj][0], lo[cj][1], hi[cj][1]);
+        *reinterpret_cast<uint16_t*>(oscales + lc * kTRG + 2 * wave) =
+            (uint16_t)(by[cj][0] | (by[cj][1] << 8));
+    }
+    __syncthreads();
+    const int64_t rgs = rows / 16, rgt = rt * kTRG;  // row-groups in all, first of the tile
+    if (wide_out) {
+        // whole tiles down every column and 16-byte aligned codes, 8-byte
+        // aligned scales: each column's 64 code bytes and 8 scale bytes are
+        // aligned too
+#pragma unroll
+        for (int k = 0; k < kTC * 4 / kThreads; k++) {
+            const int i = k * kThreads + tid;
+            const int lc = i / 4, part = i % 4;
+            const int64_t c = c0 + lc;
+            if (c < cols)
+                *reinterpret_cast<uint4*>(codes + c * (rows / 2) + rgt * 8 + part * 16) =
+                    *reinterpret_cast<const uint4*>(ocodes + lc * kCodeRow + part * 16);
+        }
+        if (tid < kTC && c0 + tid < cols)
+            *reinterpret_cast<uint2*>(scales + (c0 + tid) * rgs + rgt) =
+                *reinterpret_cast<const uint2*>(oscales + tid * kTRG);
+        return;
+    }
+    // codes: 8-byte pieces, 8 per column; scales: single bytes, 8 per column
+#pragma unroll
+    for (int k = 0; k < kTC * kTRG / kThreads; k++) {
+        const int i = k * kThreads + tid;
+        const int lc = i / kTRG, part = i % kTRG;
+        const int64_t c = c0 + lc, rg = rgt + part;
+        if (c < cols && rg < rgs) {
+            *reinterpret_cast<uint2*>(codes + c * (rows / 2) + rg * 8) =
+                *reinterpret_cast<const uint2*>(ocodes + lc * kCodeRow + part * 8);
+            scales[c * rgs + rg] = oscales[lc * kTRG + part];
+        }
+    }
+}
+
 template <bool kBf16, int kMode>
 hipError_t launch_t(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                     uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
+    const float pe = pow2f(scale_exp), pn = pow2f(-scale_exp);
+    const int elem = kBf16 ? 2 : 4;
+    // the tiled kernel: 16-byte aligned rows, row strides below 16 MB (its
+    // interior tiles address with 32-bit offsets)
+    if ((uintptr_t)x % 16 == 0 && (ld_x * elem) % 16 == 0 && ld_x * elem < (1 << 24)) {
+        const int64_t col_tiles = (cols + kTC - 1) / kTC, row_tiles = (rows + kTR - 1) / kTR;
+        if (col_tiles * row_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+        const int wide_out =
+            rows % kTR == 0 && (uintptr_t)codes % 16 == 0 && (uintptr_t)scales % 8 == 0;
+        hipLaunchKernelGGL((quantize_t_tile_kernel<kBf16, kMode>),
+                           dim3((unsigned)(col_tiles * row_tiles)), dim3(kThreads), 0, stream, x,
+                           rows, cols, ld_x, codes, scales, pe, pn, col_tiles, wide_out);
+        return hipGetLastError();
+    }
     const int64_t col_blocks = (cols + kThreads - 1) / kThreads;
     const int64_t chunks = (rows / 16 + kTChunk - 1) / kTChunk;
     if (col_blocks * chunks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((quantize_t_kernel<kBf16, kMode>), dim3((unsigned)(col_blocks * chunks)),
-                       dim3(kThreads), 0, stream, x, rows, cols, ld_x, codes, scales,
-                       pow2f(scale_exp), pow2f(-scale_exp), col_blocks);
+                       dim3(kThreads), 0, stream, x, rows, cols, ld_x, codes, scales, pe, pn,
+                       col_blocks);
     return hipGetLastError();
 }
 

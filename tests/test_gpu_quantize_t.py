@@ -13,16 +13,19 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def gpu_qt(x, e, mode=0, dtype="bf16", ld=None):
+def gpu_qt(x, e, mode=0, dtype="bf16", ld=None, offset=0):
+    """x on the GPU as a [rows, cols] view with leading dimension ld, starting
+    `offset` elements into its allocation (offset 1 breaks 16-byte alignment)."""
     from adaptive_block_scaled_amd import if4
     rows, cols = x.shape
     t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     if dtype == "bf16":
         t = t.to(torch.bfloat16)
-    if ld is not None:
-        big = torch.zeros((rows, ld), dtype=t.dtype, device="cuda")
-        big[:, :cols] = t
-        t = big[:, :cols]
+    if ld is not None or offset:
+        ld = cols if ld is None else ld
+        big = torch.zeros((rows, ld + offset), dtype=t.dtype, device="cuda")
+        big[:, offset:offset + cols] = t
+        t = big[:, offset:offset + cols]
     c, s = if4.quantize_t(t, e, mode)
     torch.cuda.synchronize()
     return c.cpu().numpy(), s.cpu().numpy()
@@ -48,6 +51,28 @@ def test_matches_quantize_of_transpose(oracle_mod, shape, dtype):
     gc, gs = gpu_qt(x, e, 0, dtype, ld=cols + 24)
     rc, rs = oracle_qt(oracle_mod, x, e, 0)
     assert np.array_equal(gc, rc) and np.array_equal(gs, rs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape,ld,offset", [
+    ((144, 130), 136, 0),   # 16-byte rows: LDS-tiled kernel, ragged last tile both ways
+    ((256, 200), 200, 0),   # whole row tiles: the aligned 16-byte column stores
+    ((48, 3), 8, 0),        # a single partial 16-byte chunk per row
+    ((400, 270), 272, 0),   # several tiles, 2-element tail chunk
+    ((144, 130), 136, 1),   # misaligned start: per-element kernel
+    ((32, 300), 300, 0),    # bf16 rows of 600 bytes: per-element kernel
+])
+def test_tiled_and_per_element_paths(oracle_mod, dtype, shape, ld, offset):
+    rows, cols = shape
+    x = wl.outlier_activations(rows, cols, 7 * rows + cols)
+    if dtype == "bf16":
+        x = wl.to_bf16_f32(x)
+    e = wl.tensor_scale_exp(float(np.abs(x).max()))
+    print(f"[quantize_t] {dtype} {rows}x{cols} ld={ld} offset={offset} E={e}", flush=True)
+    for mode in (0, 2):
+        gc, gs = gpu_qt(x, e, mode, dtype, ld=ld, offset=offset)
+        rc, rs = oracle_qt(oracle_mod, x, e, mode)
+        assert np.array_equal(gc, rc) and np.array_equal(gs, rs), (mode, shape, ld, offset)
 
 
 def test_full_size_weight(oracle_mod):
