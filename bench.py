@@ -9,10 +9,14 @@ GEMM C[8192, 28672] = A W^T in fp32.  Inputs are resident in HBM before the
 timed region.  `value` is the step's throughput counted as the GEMM's
 2*M*N*K flops per step time (TFLOP/s); per-kernel figures (quantize GB/s
 against the 8 TB/s HBM peak, GEMM TFLOP/s against the 2.5 PFLOP/s dense
-fp16 MFMA peak, and the dequantize kernel timed after the step loop) are in
-`kernels`, and `roofline` reports the dominant kernel.  `kernels` also
-holds a plain device-to-device copy of W's input, timed the same way, as the
-practical HBM reference for the memory-bound kernels (`frac_of_copy`).
+fp16 MFMA peak) are in `kernels`, and `roofline` reports the dominant
+kernel.  After the step loop, three more kernels are timed on W's 470 MB,
+beyond the 256 MB last-level cache, and reported in `kernels` only: the
+dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0)
+and the quantize after a random-sign 16-point Hadamard rotation of each
+group.  `kernels` also holds a plain device-to-device copy of W's input,
+timed the same way, as the practical HBM reference for the memory-bound
+kernels (`frac_of_copy`).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -158,6 +162,27 @@ def main():
     torch.cuda.synchronize()
     ms_deq = ev_d[0].elapsed_time(ev_d[1]) / nd
 
+    # the widened rows, timed the same way on W (beyond the last-level cache):
+    # quantize of W^T (groups along dim 0, the backward products' layout) and
+    # the random-sign Hadamard rotation fused into the quantize
+    def time_launches(fn, n=10):
+        for _ in range(2):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    wtc = torch.empty((K, N // 2), dtype=torch.uint8, device=dev)
+    wts = torch.empty((K, N // 16), dtype=torch.uint8, device=dev)
+    ms_qt = time_launches(lambda: if4.quantize_t(W, ew, out=(wtc, wts)))
+    del wtc, wts
+    mask = wl.sign_mask(wl.random_signs(np.random.default_rng(0)))
+    ms_rht = time_launches(lambda: if4.quantize_rht(W, mask, ew + 2, out=(wc, ws)))
+
     # practical HBM reference: a plain device-to-device copy of W's bf16 input
     # (reads and writes the same number of bytes), timed like the kernels
     Wc = torch.empty_like(W)
@@ -202,6 +227,14 @@ def main():
                               "GB/s": round(deq_gbs, 1),
                               "frac_hbm_peak": round(deq_gbs / HBM_PEAK_GBS, 4),
                               "frac_of_copy": round(deq_gbs / copy_gbs, 4)},
+        "quantize_t_W": {"ms": round(ms_qt, 4), "bytes": qw_b,
+                         "GB/s": round(qw_b / (ms_qt * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(qw_b / (ms_qt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "frac_of_copy": round(qw_b / (ms_qt * 1e-3) / 1e9 / copy_gbs, 4)},
+        "quantize_rht_W": {"ms": round(ms_rht, 4), "bytes": qw_b,
+                           "GB/s": round(qw_b / (ms_rht * 1e-3) / 1e9, 1),
+                           "frac_hbm_peak": round(qw_b / (ms_rht * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "frac_of_copy": round(qw_b / (ms_rht * 1e-3) / 1e9 / copy_gbs, 4)},
         "hbm_copy_reference": {"bytes": copy_bytes, "GB/s": round(copy_gbs, 1),
                                "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
     }
