@@ -395,3 +395,209 @@ void if4o_quantize_rht(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
         }
     }
 }
+
+/* ------------------------------------------------------------------------
+ * IF3 and IF6: the same adaptive choice at 3 and 6 bits per value ([podcast]
+ * "It Generalizes: IF3 and IF6"; [gist] section 2, "Extensoes").  The pages
+ * name the formats but define neither grid; the readings here keep IF4's
+ * construction -- sign-magnitude codes, one E4M3 scale per 16 values with the
+ * choice in its sign bit, the INT range pre-scaled so that its top value
+ * lands on the float grid's top value, scale = RNE_E4M3(amax / top), errors
+ * compared in fp32 in a domain where the INT descale is exact:
+ *   IF6: FP6 = E2M3 (2 exponent bits, bias 1, 3 mantissa bits; top 7.5), INT6
+ *        magnitudes 0..31 decoding to q * 7.5/31 * s = q * 15/62 * s; errors
+ *        in the x62 domain.
+ *   IF3: FP3 = E2M0 (magnitudes 0, 1, 2, 4; top 4), INT3 magnitudes 0..3
+ *        decoding to q * 4/3 * s; errors in the x3 domain.  (The other 2-bit
+ *        float, E1M1 = {0, 0.5, 1, 1.5}, is the INT grid itself and would
+ *        leave no choice.)
+ * Codes: bit (bits - 1) = sign of x, the low bits = FP index or |q|; element i
+ * of a group occupies bits [bits*i, bits*(i+1)) of the group's little-endian
+ * 2*bits-byte field. */
+typedef struct {
+    int bits;
+    const double* fp;
+    unsigned nfp;   /* 2^(bits-1) float magnitudes */
+    unsigned qmax;  /* 2^(bits-1) - 1 */
+    double top;     /* fp[nfp - 1] */
+    double dn, dd;  /* top / qmax = dn / dd in lowest terms */
+} ifn_format;
+
+static double E2M3[32];
+static const double E2M0[4] = {0.0, 1.0, 2.0, 4.0};
+static double INT_MAG[32];
+
+__attribute__((constructor)) static void fill_ifn_grids(void) {
+    for (unsigned c = 0; c < 32; c++) {
+        unsigned e = c >> 3, m = c & 7u;
+        E2M3[c] = e == 0 ? m / 8.0 : ldexp(1.0 + m / 8.0, (int)e - 1);
+        INT_MAG[c] = (double)c;
+    }
+}
+
+static int ifn_get(int bits, ifn_format* f) {
+    if (bits == 6) {
+        *f = (ifn_format){6, E2M3, 32, 31, 7.5, 15.0, 62.0};
+        return 0;
+    }
+    if (bits == 3) {
+        *f = (ifn_format){3, E2M0, 4, 3, 4.0, 4.0, 3.0};
+        return 0;
+    }
+    return -1;
+}
+
+double if4o_ifn_fp_value(int bits, unsigned idx) {
+    ifn_format f;
+    if (ifn_get(bits, &f)) return NAN;
+    return f.fp[idx % f.nfp];
+}
+
+unsigned if4o_ifn_scale_code(int bits, double a_scaled) {
+    ifn_format f;
+    if (ifn_get(bits, &f)) return 0;
+    /* a vs top * midpoint: top has at most 4 bits, the midpoints 5 */
+    return rne_index(a_scaled, f.top, e4m3_grid(), 127);
+}
+
+unsigned if4o_ifn_fp_index(int bits, double ax, double s) {
+    ifn_format f;
+    if (ifn_get(bits, &f)) return 0;
+    return rne_index(ax, s, f.fp, f.nfp);
+}
+
+unsigned if4o_ifn_int_mag(int bits, double ax, double s) {
+    ifn_format f;
+    if (ifn_get(bits, &f)) return 0;
+    /* q = RNE(dd |x| / (dn s)), clamped: dd |x| vs dn s (k + 1/2), exact */
+    return rne_index(f.dd * ax, f.dn * s, INT_MAG, f.qmax + 1);
+}
+
+static void ifn_quantize_group(const ifn_format* f, const float x[16], int32_t scale_exp,
+                               int mode, unsigned code[16], uint8_t* scale_byte, float* err_fp,
+                               float* err_int) {
+    for (int i = 0; i < GROUP; i++) code[i] = 0;
+    *err_fp = 0.0f;
+    *err_int = 0.0f;
+    for (int i = 0; i < GROUP; i++) {
+        if (!isfinite(x[i])) {
+            *scale_byte = 0x7F;
+            return;
+        }
+    }
+    double a = 0.0;
+    for (int i = 0; i < GROUP; i++) {
+        double ax = fabs((double)x[i]);
+        if (ax > a) a = ax;
+    }
+    unsigned sc = rne_index(ldexp(a, -scale_exp), f->top, e4m3_grid(), 127);
+    if (sc == 0) {
+        *scale_byte = 0;
+        return;
+    }
+    double s = ldexp(if4o_e4m3_value(sc), scale_exp);
+    unsigned fidx[GROUP], qmag[GROUP];
+    for (int i = 0; i < GROUP; i++) {
+        double ax = fabs((double)x[i]);
+        fidx[i] = rne_index(ax, s, f->fp, f->nfp);
+        qmag[i] = rne_index(f->dd * ax, f->dn * s, INT_MAG, f->qmax + 1);
+    }
+    /* errors in the x dd domain, fp32, index order, one fma per element:
+     * d = fma(|x|, dd, -c dd s) and fma(|x|, dd, -|q| dn s); the products
+     * c*dd*s and |q|*dn*s have at most 13 bits and are exact in fp32 */
+    float sf = (float)s, fdd = (float)f->dd, fdn = (float)f->dn;
+    float ef = 0.0f, ei = 0.0f;
+    for (int i = 0; i < GROUP; i++) {
+        float ax = fabsf(x[i]);
+        float cs = (float)f->fp[fidx[i]] * fdd * sf;
+        float qs = (float)qmag[i] * fdn * sf;
+        float df = fmaf(ax, fdd, -cs);
+        float di = fmaf(ax, fdd, -qs);
+        ef = fmaf(df, df, ef);
+        ei = fmaf(di, di, ei);
+    }
+    *err_fp = ef;
+    *err_int = ei;
+    int use_int = mode == IF4O_FORCE_INT4 ? 1 : (mode == IF4O_FORCE_FP4 ? 0 : ei < ef);
+    *scale_byte = (uint8_t)(sc | (use_int ? 0x80u : 0u));
+    for (int i = 0; i < GROUP; i++) {
+        unsigned mag = use_int ? qmag[i] : fidx[i];
+        code[i] = (signbit(x[i]) ? (1u << (f->bits - 1)) : 0u) | mag;
+    }
+}
+
+static void ifn_pack(int bits, const unsigned code[16], uint8_t* out) {
+    for (int b = 0; b < 2 * bits; b++) out[b] = 0;
+    for (int i = 0; i < GROUP; i++)
+        for (int k = 0; k < bits; k++)
+            if ((code[i] >> k) & 1u) {
+                int bit = bits * i + k;
+                out[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+            }
+}
+
+static unsigned ifn_unpack(int bits, const uint8_t* in, int i) {
+    unsigned v = 0;
+    for (int k = 0; k < bits; k++) {
+        int bit = bits * i + k;
+        v |= (unsigned)((in[bit >> 3] >> (bit & 7)) & 1u) << k;
+    }
+    return v;
+}
+
+int if4o_ifn_quantize(int bits, const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                      int32_t scale_exp, int mode, uint8_t* codes, uint8_t* scales,
+                      float* err_fp, float* err_int, int nthreads) {
+    ifn_format f;
+    if (ifn_get(bits, &f) || cols % GROUP) return -1;
+    int64_t gpr = cols / GROUP, cb = gpr * 2 * bits;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t g = 0; g < gpr; g++) {
+            unsigned code[GROUP];
+            float ef, ei;
+            ifn_quantize_group(&f, x + r * ld_x + g * GROUP, scale_exp, mode, code,
+                               scales + r * gpr + g, &ef, &ei);
+            ifn_pack(bits, code, codes + r * cb + g * 2 * bits);
+            if (err_fp) err_fp[r * gpr + g] = ef;
+            if (err_int) err_int[r * gpr + g] = ei;
+        }
+    }
+    return 0;
+}
+
+/* Dequantize: FP -> sign * fp[idx] * s' * 2^E (exact); INT -> sign *
+ * fl32(|q| dn s' / dd) * 2^E: |q| dn s' has at most 13 bits, so the fp64
+ * quotient is never within 2^-53 of an fp32 midpoint and the two roundings
+ * equal one. */
+int if4o_ifn_dequantize(int bits, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                        int64_t cols, int32_t scale_exp, float* y, int64_t ld_y, int nthreads) {
+    ifn_format f;
+    if (ifn_get(bits, &f) || cols % GROUP) return -1;
+    int64_t gpr = cols / GROUP, cb = gpr * 2 * bits;
+    float p2 = ldexpf(1.0f, scale_exp);
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t k = 0; k < cols; k++) {
+            int64_t g = k / GROUP;
+            unsigned b = scales[r * gpr + g];
+            unsigned code = ifn_unpack(bits, codes + r * cb + g * 2 * bits, (int)(k % GROUP));
+            unsigned mag = code & ((1u << (bits - 1)) - 1u);
+            double sp = if4o_e4m3_value(b & 0x7Fu);
+            float v;
+            if (b & 0x80u)
+                v = (float)((mag * f.dn * sp) / f.dd);
+            else
+                v = (float)(f.fp[mag] * sp);
+            if ((code >> (bits - 1)) & 1u) v = -v;
+            y[r * ld_y + k] = v * p2;
+        }
+    }
+    return 0;
+}

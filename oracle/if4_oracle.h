@@ -16,7 +16,8 @@
  *             "方法详解" (method details) -- technical framework steps 1-5,
  *             key design; and the English abstract.
  *   [podcast] "Adaptive Block-Scaled Data Types for FP4 Training", episode
- *             companion: "One Group, Two Candidate Encodings", "The Free Bit:
+ *             companion: "It Generalizes: IF3 and IF6", "One Group, Two
+ *             Candidate Encodings", "The Free Bit:
  *             Scale Factor Sign", "MAC Unit: Decoding Two Formats from One
  *             Sign Bit", "Where the Gain Actually Comes From" (the
  *             Hadamard-transformed weight gradient).
@@ -30,7 +31,9 @@
  * Pins: every function here is checked by the CPU tests against closed forms,
  * exhaustive brute force and an exact-rational re-implementation (see
  * tests/test_oracle_pins.py); the Hadamard rotation against scipy's Sylvester
- * matrix, its error bound and hand-worked fp32 groups (tests/test_oracle_rht.py).
+ * matrix, its error bound and hand-worked fp32 groups (tests/test_oracle_rht.py);
+ * IF3 / IF6 against their grids' bit layouts, exhaustive exact-rational
+ * roundings and an independent exact statement of groups (tests/test_oracle_ifn.py).
  */
 #ifndef IF4_ORACLE_H
 #define IF4_ORACLE_H
@@ -112,6 +115,21 @@ void if4o_rht16(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
 void if4o_quantize_rht(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
                        uint32_t sign_mask, int round_to_bf16, int32_t scale_exp,
                        int mode, uint8_t* codes, uint8_t* scales, int nthreads);
+
+/* IF3 / IF6 (bits = 3 or 6; see the .c file for the readings).  Codes are
+ * [rows, cols/16 * 2*bits] bytes (element i of a group at bits
+ * [bits*i, bits*(i+1)) of its little-endian field), scales [rows, cols/16];
+ * mode as for IF4 (FORCE_FP4 = force the float format, FORCE_INT4 = force
+ * INT).  Return 0, or -1 for an unknown width or cols % 16 != 0. */
+double if4o_ifn_fp_value(int bits, unsigned idx);
+unsigned if4o_ifn_scale_code(int bits, double a_scaled);
+unsigned if4o_ifn_fp_index(int bits, double ax, double s);
+unsigned if4o_ifn_int_mag(int bits, double ax, double s);
+int if4o_ifn_quantize(int bits, const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                      int32_t scale_exp, int mode, uint8_t* codes, uint8_t* scales,
+                      float* err_fp, float* err_int, int nthreads);
+int if4o_ifn_dequantize(int bits, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                        int64_t cols, int32_t scale_exp, float* y, int64_t ld_y, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,20 @@ def lib():
         L.if4o_quantize_rht.restype = None
         L.if4o_quantize_rht.argtypes = [c_f32p, i64, i64, i64, ctypes.c_uint32, ctypes.c_int,
                                         i32, ctypes.c_int, c_u8p, c_u8p, ctypes.c_int]
+        L.if4o_ifn_fp_value.restype = ctypes.c_double
+        L.if4o_ifn_fp_value.argtypes = [ctypes.c_int, ctypes.c_uint]
+        L.if4o_ifn_scale_code.restype = ctypes.c_uint
+        L.if4o_ifn_scale_code.argtypes = [ctypes.c_int, ctypes.c_double]
+        L.if4o_ifn_fp_index.restype = ctypes.c_uint
+        L.if4o_ifn_fp_index.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.if4o_ifn_int_mag.restype = ctypes.c_uint
+        L.if4o_ifn_int_mag.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.if4o_ifn_quantize.restype = ctypes.c_int
+        L.if4o_ifn_quantize.argtypes = [ctypes.c_int, c_f32p, i64, i64, i64, i32, ctypes.c_int,
+                                        c_u8p, c_u8p, c_f32p, c_f32p, ctypes.c_int]
+        L.if4o_ifn_dequantize.restype = ctypes.c_int
+        L.if4o_ifn_dequantize.argtypes = [ctypes.c_int, c_u8p, c_u8p, i64, i64, i32, c_f32p, i64,
+                                          ctypes.c_int]
         _lib = L
     return _lib
 
@@ -186,3 +200,54 @@ def quantize_rht(x, sign_mask: int, scale_exp: int = 0, mode: int = ADAPTIVE,
                             int(round_to_bf16), scale_exp, mode, _ptr(codes, ctypes.c_uint8),
                             _ptr(scales, ctypes.c_uint8), nthreads)
     return codes, scales
+
+
+def ifn_fp_value(bits: int, idx: int) -> float:
+    return lib().if4o_ifn_fp_value(bits, idx)
+
+
+def ifn_scale_code(bits: int, a_scaled: float) -> int:
+    return lib().if4o_ifn_scale_code(bits, float(a_scaled))
+
+
+def ifn_fp_index(bits: int, ax: float, s: float) -> int:
+    return lib().if4o_ifn_fp_index(bits, float(ax), float(s))
+
+
+def ifn_int_mag(bits: int, ax: float, s: float) -> int:
+    return lib().if4o_ifn_int_mag(bits, float(ax), float(s))
+
+
+def quantize_ifn(x, bits: int, scale_exp: int = 0, mode: int = ADAPTIVE,
+                 with_errors: bool = False, nthreads: int = 0):
+    """IF3 (bits=3) or IF6 (bits=6) of float32 x [rows, cols]: codes uint8
+    [rows, cols/16 * 2*bits], scales uint8 [rows, cols/16] (and the fp32
+    error sums when with_errors)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    assert cols % GROUP == 0 and bits in (3, 6)
+    codes = np.zeros((rows, cols // GROUP * 2 * bits), np.uint8)
+    scales = np.zeros((rows, cols // GROUP), np.uint8)
+    ef = np.zeros((rows, cols // GROUP), np.float32) if with_errors else None
+    ei = np.zeros((rows, cols // GROUP), np.float32) if with_errors else None
+    st = lib().if4o_ifn_quantize(bits, _ptr(x, ctypes.c_float), rows, cols, cols, scale_exp, mode,
+                                 _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
+                                 _ptr(ef, ctypes.c_float) if with_errors else None,
+                                 _ptr(ei, ctypes.c_float) if with_errors else None, nthreads)
+    assert st == 0
+    if with_errors:
+        return codes, scales, ef, ei
+    return codes, scales
+
+
+def dequantize_ifn(codes, scales, bits: int, scale_exp: int = 0, nthreads: int = 0):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, gpr = scales.shape
+    cols = gpr * GROUP
+    assert codes.shape == (rows, gpr * 2 * bits)
+    y = np.zeros((rows, cols), np.float32)
+    st = lib().if4o_ifn_dequantize(bits, _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
+                                   rows, cols, scale_exp, _ptr(y, ctypes.c_float), cols, nthreads)
+    assert st == 0
+    return y
