@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libif4.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "dequantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "dequantize.hip", "gemm.hip", "ifn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -99,6 +99,32 @@ int if4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                              IF4_MODE_ADAPTIVE, stream);
 }
 
+int if4_quantize_ifn(int bits, const void* x, int x_dtype, int64_t rows, int64_t cols,
+                     int64_t ld_x, uint8_t* codes, uint8_t* scales, int32_t scale_exp, int mode,
+                     void* stream) {
+    if (bits != 3 && bits != 6) return IF4_ERR_DTYPE;
+    int st = check_quantize(x, x_dtype, rows, cols, ld_x, codes, scales, scale_exp, mode);
+    if (st != IF4_OK || rows == 0 || cols == 0) return st;
+    return hip_status(if4::launch_quantize_ifn(bits, x, x_dtype == IF4_BF16, rows, cols, ld_x,
+                                               codes, scales, scale_exp, mode,
+                                               (hipStream_t)stream));
+}
+
+int if4_dequantize_ifn(int bits, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                       int64_t cols, int32_t scale_exp, void* y, int y_dtype, int64_t ld_y,
+                       void* stream) {
+    if (bits != 3 && bits != 6) return IF4_ERR_DTYPE;
+    if (y_dtype != IF4_F32 && y_dtype != IF4_BF16) return IF4_ERR_DTYPE;
+    if (rows < 0 || cols < 0 || cols % 16 != 0 || ld_y < cols) return IF4_ERR_SHAPE;
+    if (scale_exp < -kMaxExp || scale_exp > kMaxExp) return IF4_ERR_RANGE;
+    if (rows == 0 || cols == 0) return IF4_OK;
+    if (!codes || !scales || !y) return IF4_ERR_NULL;
+    if (!aligned(y, 16) || (ld_y * elem_size(y_dtype)) % 16 != 0 || !aligned(codes, 8))
+        return IF4_ERR_ALIGN;
+    return hip_status(if4::launch_dequantize_ifn(bits, codes, scales, rows, cols, scale_exp, y,
+                                                 y_dtype == IF4_BF16, ld_y, (hipStream_t)stream));
+}
+
 int if4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                    int64_t cols, int32_t scale_exp, void* y, int y_dtype,
                    int64_t ld_y, void* stream) {

@@ -34,6 +34,14 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
                              int64_t rows, int64_t cols, int32_t scale_exp,
                              void* y, int bf16, int64_t ld_y, hipStream_t stream);
 
+hipError_t launch_quantize_ifn(int bits, const void* x, int bf16, int64_t rows, int64_t cols,
+                               int64_t ld_x, uint8_t* codes, uint8_t* scales, int32_t scale_exp,
+                               int mode, hipStream_t stream);
+
+hipError_t launch_dequantize_ifn(int bits, const uint8_t* codes, const uint8_t* scales,
+                                 int64_t rows, int64_t cols, int32_t scale_exp, void* y, int bf16,
+                                 int64_t ld_y, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        int32_t a_exp, const uint8_t* w_codes,
                        const uint8_t* w_scales, int32_t w_exp, int64_t M,

@@ -20,7 +20,8 @@ MODE_ADAPTIVE, MODE_FORCE_FP4, MODE_FORCE_INT4 = 0, 1, 2
 GROUP = 16
 
 EXPORTS = ("if4_version", "if4_status_string", "if4_quantize", "if4_quantize_mode",
-           "if4_quantize_t", "if4_quantize_rht", "if4_dequantize", "if4_gemm")
+           "if4_quantize_t", "if4_quantize_rht", "if4_quantize_ifn", "if4_dequantize",
+           "if4_dequantize_ifn", "if4_gemm")
 
 
 class IF4Error(RuntimeError):
@@ -46,6 +47,10 @@ def _load():
     L.if4_quantize_mode.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
     L.if4_quantize_t.restype = ci
     L.if4_quantize_t.argtypes = [vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
+    L.if4_quantize_ifn.restype = ci
+    L.if4_quantize_ifn.argtypes = [ci, vp, ci, i64, i64, i64, vp, vp, i32, ci, vp]
+    L.if4_dequantize_ifn.restype = ci
+    L.if4_dequantize_ifn.argtypes = [ci, vp, vp, i64, i64, i32, vp, ci, i64, vp]
     L.if4_quantize_rht.restype = ci
     L.if4_quantize_rht.argtypes = [vp, ci, i64, i64, i64, ctypes.c_uint32, vp, vp, i32, ci, vp]
     L.if4_dequantize.restype = ci
@@ -140,6 +145,40 @@ def quantize_rht(x: torch.Tensor, sign_mask: int, scale_exp: int = 0, mode: int 
                               int(scale_exp), int(mode), _stream(x.device))
     _check("if4_quantize_rht", st)
     return codes, scales
+
+
+def quantize_ifn(x: torch.Tensor, bits: int, scale_exp: int = 0, mode: int = MODE_ADAPTIVE,
+                 out=None):
+    """IF3 (bits=3) or IF6 (bits=6) of a 2-D CUDA tensor (groups of 16 along
+    dim 1).  Returns (codes uint8 [rows, cols/16 * 2*bits], scales uint8
+    [rows, cols/16])."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor with unit stride along dim 1")
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty((rows, cols // GROUP * 2 * bits), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // GROUP), dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    st = lib.if4_quantize_ifn(int(bits), x.data_ptr(), _dtype_code(x.dtype), rows, cols,
+                              x.stride(0), codes.data_ptr(), scales.data_ptr(), int(scale_exp),
+                              int(mode), _stream(x.device))
+    _check("if4_quantize_ifn", st)
+    return codes, scales
+
+
+def dequantize_ifn(codes: torch.Tensor, scales: torch.Tensor, bits: int, scale_exp: int = 0,
+                   dtype=torch.float32, out=None) -> torch.Tensor:
+    rows, gpr = scales.shape
+    cols = gpr * GROUP
+    if codes.shape != (rows, gpr * 2 * bits):
+        raise ValueError("codes must be [rows, cols/16 * 2*bits]")
+    y = torch.empty((rows, cols), dtype=dtype, device=codes.device) if out is None else out
+    st = lib.if4_dequantize_ifn(int(bits), codes.data_ptr(), scales.data_ptr(), rows, cols,
+                                int(scale_exp), y.data_ptr(), _dtype_code(y.dtype), y.stride(0),
+                                _stream(codes.device))
+    _check("if4_dequantize_ifn", st)
+    return y
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, scale_exp: int = 0,

@@ -126,6 +126,47 @@ int if4_quantize_rht(const void* x, int x_dtype, int64_t rows, int64_t cols,
                      uint8_t* scales, int32_t scale_exp, int mode, void* stream);
 
 /*
+ * IF3 and IF6: the adaptive per-group choice at 3 and 6 bits per value
+ * ("Adaptive Block-Scaled Data Types for FP4 Training", podcast companion,
+ * "It Generalizes: IF3 and IF6"; gist.science summary, section 2,
+ * "Extensoes").  The pages name the formats without defining them; these
+ * keep IF4's construction:
+ *   bits = 6 (IF6): float candidate FP6 E2M3 (2 exponent bits, bias 1,
+ *     3 mantissa bits, subnormals; top 7.5); INT candidate |q| <= 31,
+ *     decoding to q * (15/62) * s so that 31 lands on 7.5.
+ *   bits = 3 (IF3): float candidate FP3 E2M0 (magnitudes 0, 1, 2, 4);
+ *     INT candidate |q| <= 3, decoding to q * (4/3) * s.
+ * Per group of 16 along dim 1: scale s' = RNE_E4M3(amax * 2^-E / top) with
+ * top = 7.5 or 4 (saturating at 448; 0 gives the zero group), s = s' 2^E;
+ * float code = RNE index on the grid (ties to the even index, saturating);
+ * INT |q| = min(RNE(|x| / (step s)), qmax) with step = top / qmax; squared
+ * errors summed in fp32 in index order as e = fma(d, d, e), with
+ * d = fma(|x|, dd, -c dd s) for the float code and fma(|x|, dd, -|q| dn s)
+ * for INT, where top / qmax = dn / dd in lowest terms (15/62, 4/3); INT is
+ * kept iff its sum is strictly lower (mode as for if4_quantize_mode); the
+ * scale byte is s' | flag << 7, 0x7F for a group holding NaN or infinity.
+ * Codes: bit (bits - 1) = sign of x, low bits = float index or |q|; element i
+ * of a group occupies bits [bits*i, bits*(i+1)) of the group's
+ * little-endian field of 2*bits bytes.
+ *   codes   device [rows, cols/16 * 2*bits] bytes, 8-byte aligned
+ *   scales  device [rows, cols/16]
+ *   bits    3 or 6 (else IF4_ERR_DTYPE)
+ * Other arguments, alignment and errors as if4_quantize_mode.
+ */
+int if4_quantize_ifn(int bits, const void* x, int x_dtype, int64_t rows, int64_t cols,
+                     int64_t ld_x, uint8_t* codes, uint8_t* scales, int32_t scale_exp, int mode,
+                     void* stream);
+
+/* Dequantize IF3 / IF6 codes (layout as if4_quantize_ifn): float codes to
+ * sign * grid value * s' * 2^E, INT codes to sign * (the fp32 nearest
+ * |q| * dn * s' / dd) * 2^E; y as for if4_dequantize (fp32 or bf16, rounded
+ * to nearest even).  codes 8-byte aligned; errors as if4_dequantize, plus
+ * IF4_ERR_DTYPE for bits other than 3 and 6. */
+int if4_dequantize_ifn(int bits, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                       int64_t cols, int32_t scale_exp, void* y, int y_dtype, int64_t ld_y,
+                       void* stream);
+
+/*
  * Quantize x^T: the groups are 16 consecutive ROWS of each column of x, and
  * the result is bit for bit if4_quantize_mode applied to the transpose of x
  * (same rules, same mode).  This is the operand layout the backward products

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert names == sorted(["if4_version", "if4_status_string", "if4_quantize",
                             "if4_quantize_mode", "if4_quantize_t", "if4_quantize_rht",
-                            "if4_dequantize", "if4_gemm"])
+                            "if4_quantize_ifn", "if4_dequantize", "if4_dequantize_ifn",
+                            "if4_gemm"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -103,6 +104,30 @@ def test_quantize_rht_validation(L):
     assert qr(L, ld=36) == 3           # 72-byte rows break 16-byte alignment
     assert qr(L, codes=FAKE + 4) == 3
     assert qr(L, rows=0) == 0 and qr(L, cols=0, ld=0) == 0
+
+
+def qn(L, bits=6, x=FAKE, dt=1, rows=4, cols=32, ld=32, codes=FAKE, scales=FAKE, e=0, mode=0):
+    return L.if4_quantize_ifn(bits, x, dt, rows, cols, ld, codes, scales, e, mode, None)
+
+
+def dn(L, bits=6, codes=FAKE, scales=FAKE, rows=4, cols=32, e=0, y=FAKE, dt=1, ld=32):
+    return L.if4_dequantize_ifn(bits, codes, scales, rows, cols, e, y, dt, ld, None)
+
+
+def test_ifn_validation(L):
+    # every call below has exactly one bad argument, so none launches
+    for b in (0, 4, 5, 8):
+        assert qn(L, bits=b) == 4 and dn(L, bits=b) == 4
+    assert qn(L, dt=2) == 4 and qn(L, mode=3) == 4
+    assert qn(L, cols=40, ld=40) == 2 and qn(L, ld=16) == 2
+    assert qn(L, e=65) == 5
+    assert qn(L, x=None) == 1 and qn(L, codes=None) == 1
+    assert qn(L, x=FAKE + 2) == 3 and qn(L, codes=FAKE + 4) == 3
+    assert qn(L, rows=0) == 0 and qn(L, bits=3, cols=0, ld=0) == 0
+    assert dn(L, dt=5) == 4 and dn(L, cols=20, ld=32) == 2 and dn(L, ld=16) == 2
+    assert dn(L, e=-65) == 5 and dn(L, y=None) == 1 and dn(L, scales=None) == 1
+    assert dn(L, y=FAKE + 8) == 3 and dn(L, codes=FAKE + 4) == 3
+    assert dn(L, rows=0) == 0
 
 
 def test_dequantize_validation(L):

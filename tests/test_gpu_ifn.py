@@ -1,0 +1,150 @@
+"""GPU parity of IF3 / IF6 (if4_quantize_ifn, if4_dequantize_ifn through the
+C ABI) against the CPU oracle: codes, scale bytes and decoded values bit for
+bit."""
+import numpy as np
+import pytest
+
+from adaptive_block_scaled_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _if4():
+    from adaptive_block_scaled_amd import if4
+    return if4
+
+
+def to_dev(x_np, dtype, ld=None):
+    rows, cols = x_np.shape
+    t = torch.from_numpy(np.ascontiguousarray(x_np))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t.float()
+    if ld is not None and ld != cols:
+        big = torch.zeros((rows, ld), dtype=t.dtype)
+        big[:, :cols] = t
+        return big.cuda()[:, :cols]
+    return t.cuda()
+
+
+def check_q(oracle_mod, x, bits, dtype, e, mode=0, ld=None, label=""):
+    print(f"[ifn] {label} IF{bits} {dtype} {x.shape} E={e} mode={mode} ld={ld}", flush=True)
+    c, s = _if4().quantize_ifn(to_dev(x, dtype, ld), bits, e, mode)
+    torch.cuda.synchronize()
+    gc, gs = c.cpu().numpy(), s.cpu().numpy()
+    oc, os_ = oracle_mod.quantize_ifn(x, bits, e, mode)
+    bad = np.nonzero(gs != os_)
+    assert np.array_equal(gs, os_), (label, bad[0][:4], bad[1][:4], gs[bad][:4], os_[bad][:4])
+    assert np.array_equal(gc, oc), label
+    return c, s
+
+
+def check_dq(oracle_mod, c, s, bits, e, label=""):
+    want = oracle_mod.dequantize_ifn(c.cpu().numpy(), s.cpu().numpy(), bits, e)
+    y32 = _if4().dequantize_ifn(c, s, bits, e, torch.float32)
+    yb = _if4().dequantize_ifn(c, s, bits, e, torch.bfloat16)
+    torch.cuda.synchronize()
+    got = y32.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)) or \
+        np.array_equal(np.isnan(got), np.isnan(want)) and \
+        np.array_equal(np.where(np.isnan(got), 0, got).view(np.uint32),
+                       np.where(np.isnan(want), 0, want).view(np.uint32)), label
+    wb = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+    gb = yb.float().cpu().numpy()
+    assert np.array_equal(np.isnan(gb), np.isnan(wb))
+    assert np.array_equal(np.where(np.isnan(gb), 0, gb).view(np.uint32),
+                          np.where(np.isnan(wb), 0, wb).view(np.uint32)), label
+
+
+def draw(shape, kind, seed, dtype):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        x = rng.standard_normal(shape)
+    elif kind == "t4":
+        x = rng.standard_t(4, shape) * 0.02
+    elif kind == "uniform":
+        x = rng.uniform(-1, 1, shape)
+    else:  # wide exponents, subnormals included
+        x = rng.standard_normal(shape) * np.exp2(rng.integers(-140, 120, shape))
+    x = x.astype(np.float32)
+    return wl.to_bf16_f32(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 16), (7, 48), (129, 1040)])
+@pytest.mark.parametrize("kind", ["normal", "t4", "uniform"])
+def test_parity_shapes_and_distributions(oracle_mod, bits, dtype, shape, kind):
+    x = draw(shape, kind, shape[0] + bits, dtype)
+    e = wl.tensor_scale_exp(float(np.abs(x).max()) * (6.0 / (7.5 if bits == 6 else 4.0)))
+    c, s = check_q(oracle_mod, x, bits, dtype, e, label=kind)
+    check_dq(oracle_mod, c, s, bits, e, label=kind)
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forced_modes(oracle_mod, bits, mode, dtype):
+    x = draw((64, 256), "normal", 9, dtype)
+    c, s = check_q(oracle_mod, x, bits, dtype, 0, mode, label="forced")
+    check_dq(oracle_mod, c, s, bits, 0)
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("e", [-64, -20, 0, 30, 64])
+def test_wide_values_and_exponents(oracle_mod, bits, dtype, e):
+    x = draw((33, 512), "wide", 11, dtype)
+    c, s = check_q(oracle_mod, x, bits, dtype, e, label="wide")
+    check_dq(oracle_mod, c, s, bits, e)
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_edge_groups_and_strided_input(oracle_mod, bits):
+    g = np.zeros((10, 16), np.float32)
+    g[1, :] = -0.0
+    g[2, 3] = np.inf
+    g[3, 9] = np.nan
+    g[4, :] = 3.0e38
+    g[5, 0] = 1e-40
+    g[6, :] = np.linspace(-7.5, 7.5, 16)
+    g[7, :] = np.linspace(-4, 4, 16)
+    g[8, :] = 2.0 ** -12
+    g[9, ::2] = 1.0
+    x = g.reshape(5, 32)
+    for dtype in ("bf16", "f32"):
+        xx = wl.to_bf16_f32(x) if dtype == "bf16" else x
+        for e in (0, -12, 20):
+            c, s = check_q(oracle_mod, xx, bits, dtype, e, label="edge")
+            check_dq(oracle_mod, c, s, bits, e)
+        check_q(oracle_mod, draw((20, 96), "t4", 3, dtype), bits, dtype, -8, ld=96 + 32,
+                label="strided")
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_dequantize_every_code(oracle_mod, bits):
+    # every code under both flags and a spread of scale bytes (NaN scale included)
+    nm = 1 << bits
+    rows = []
+    for flag in (0, 0x80):
+        for sc in (0, 1, 7, 8, 0x2B, 0x38, 0x51, 0x7E, 0x7F):
+            for start in range(0, nm, 16):
+                cs = [(start + i) % nm for i in range(16)]
+                field = sum(c << (bits * i) for i, c in enumerate(cs)).to_bytes(2 * bits, "little")
+                rows.append((list(field), sc | flag))
+    codes = torch.tensor([r[0] for r in rows], dtype=torch.uint8).cuda()
+    scales = torch.tensor([[r[1]] for r in rows], dtype=torch.uint8).cuda()
+    for e in (0, -30, 17):
+        check_dq(oracle_mod, codes, scales, bits, e, label="all codes")
+
+
+def test_full_size_activation(oracle_mod):
+    """The activation workload (8192 x 4096 bf16 with outlier columns) in IF6
+    and IF3, every group against the oracle."""
+    t = wl.c2_activations()
+    x = t.values
+    for bits in (6, 3):
+        e = wl.tensor_scale_exp(float(np.abs(x).max()) * (6.0 / (7.5 if bits == 6 else 4.0)))
+        c, s = check_q(oracle_mod, x, bits, "bf16", e, label=t.name)
+        gs = s.cpu().numpy()
+        print(f"    IF{bits} int share {float((gs >= 0x80).mean()):.3f}", flush=True)
