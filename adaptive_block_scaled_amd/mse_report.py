@@ -11,7 +11,8 @@ groups that chose INT4, and how many groups ended with a larger error than
 the better fixed format (possible only where the fp32 selection and exact
 arithmetic disagree on a near-tie).
 
-Run: `python -m adaptive_block_scaled_amd.mse_report [--configs c1,c2,...]`.
+Run: `python -m adaptive_block_scaled_amd.mse_report [--configs c1,c2,...]
+[--bits 4,3,6]` (IF3 and IF6 against their own fixed float and INT formats).
 The error arithmetic here (fp64 torch ops) is measurement, not part of the
 quantization path.
 """
@@ -59,6 +60,36 @@ def report_tensor(t: wl.Tensor, scale_exp=None, rtol: float = 1e-5) -> dict:
     }
 
 
+def report_tensor_ifn(t: wl.Tensor, bits: int, rtol: float = 1e-5) -> dict:
+    """As report_tensor for IF3 / IF6 (bits 3 or 6) against their fixed float
+    and INT formats; the exponent follows the same rule with the format's top
+    value (4 or 7.5) in place of 6."""
+    dev = torch.device("cuda:0")
+    top = 7.5 if bits == 6 else 4.0
+    amax = float(np.max(np.abs(t.values))) if t.values.size else 0.0
+    e = wl.tensor_scale_exp(amax * 6.0 / top)
+    xd = torch.from_numpy(t.values).to(dev)
+    x = xd.to(torch.bfloat16) if t.dtype == "bf16" else xd
+    sse, flags = {}, None
+    for name, mode in MODES.items():
+        codes, scales = if4.quantize_ifn(x, bits, e, mode=mode)
+        y = if4.dequantize_ifn(codes, scales, bits, e, torch.float32)
+        d = xd.to(torch.float64) - y.to(torch.float64)
+        sse[name] = (d * d).reshape(x.shape[0], -1, if4.GROUP).sum(dim=2)
+        if name == "if4":
+            flags = (scales >= 0x80)
+    best_fixed = torch.minimum(sse["fp4"], sse["int4"])
+    n = x.numel()
+    return {
+        "tensor": t.name, "format": f"IF{bits}", "scale_exp": int(e),
+        "mse_if": float(sse["if4"].sum().item() / n),
+        "mse_fp": float(sse["fp4"].sum().item() / n),
+        "mse_int": float(sse["int4"].sum().item() / n),
+        "int_share": float(flags.double().mean().item()),
+        "groups_if_above_best_fixed": int((sse["if4"] > best_fixed * (1 + rtol) + 1e-300).sum().item()),
+    }
+
+
 def config_tensors(name: str):
     if name == "c1":
         t = wl.c1_mixed_fp32()
@@ -82,7 +113,34 @@ def main(argv=None):
                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--configs", default="c1,c2,c3,c4,c5")
     p.add_argument("--json", action="store_true", help="one JSON line per tensor")
+    p.add_argument("--bits", default="4", help="comma list of widths: 4 (IF4), 3 (IF3), 6 (IF6)")
     args = p.parse_args(argv)
+    widths = [int(b) for b in args.bits.split(",")]
+    if any(b != 4 for b in widths):
+        rows, seen = [], set()
+        for c in args.configs.split(","):
+            for t, _ in config_tensors(c.strip()):
+                if t.name in seen:  # listed twice for IF4's two exponents
+                    continue
+                seen.add(t.name)
+                for b in widths:
+                    if b == 4:
+                        continue
+                    r = report_tensor_ifn(t, b)
+                    rows.append(r)
+                    if args.json:
+                        print(json.dumps(r), flush=True)
+        if not args.json:
+            print(f"{'tensor':34s} {'fmt':>4s} {'E':>4s} {'MSE IF':>11s} {'MSE FP':>11s} "
+                  f"{'MSE INT':>11s} {'IF/FP':>7s} {'IF/INT':>7s} {'INT grp':>7s} {'worse':>5s}")
+            for r in rows:
+                print(f"{r['tensor']:34s} {r['format']:>4s} {r['scale_exp']:4d} {r['mse_if']:11.4e} "
+                      f"{r['mse_fp']:11.4e} {r['mse_int']:11.4e} "
+                      f"{r['mse_if'] / r['mse_fp'] if r['mse_fp'] else float('nan'):7.4f} "
+                      f"{r['mse_if'] / r['mse_int'] if r['mse_int'] else float('nan'):7.4f} "
+                      f"{r['int_share']:7.3f} {r['groups_if_above_best_fixed']:5d}")
+        if 4 not in widths:
+            return rows
     rows = []
     for c in args.configs.split(","):
         for t, e in config_tensors(c.strip()):

@@ -12,9 +12,9 @@ against the 8 TB/s HBM peak, GEMM TFLOP/s against the 2.5 PFLOP/s dense
 fp16 MFMA peak) are in `kernels`, and `roofline` reports the dominant
 kernel.  After the step loop, three more kernels are timed on W's 470 MB,
 beyond the 256 MB last-level cache, and reported in `kernels` only: the
-dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0)
-and the quantize after a random-sign 16-point Hadamard rotation of each
-group.  `kernels` also holds a plain device-to-device copy of W's input,
+dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0),
+the quantize after a random-sign 16-point Hadamard rotation of each group,
+and the IF6 and IF3 quantizes.  `kernels` also holds a plain device-to-device copy of W's input,
 timed the same way, as the practical HBM reference for the memory-bound
 kernels (`frac_of_copy`).
 
@@ -182,6 +182,13 @@ def main():
     del wtc, wts
     mask = wl.sign_mask(wl.random_signs(np.random.default_rng(0)))
     ms_rht = time_launches(lambda: if4.quantize_rht(W, mask, ew + 2, out=(wc, ws)))
+    # IF6 and IF3 (3 and 6 bits per value) of the same weight
+    ms_ifn, bytes_ifn = {}, {}
+    for bits in (6, 3):
+        wnc = torch.empty((N, K // 16 * 2 * bits), dtype=torch.uint8, device=dev)
+        ms_ifn[bits] = time_launches(lambda: if4.quantize_ifn(W, bits, ew, out=(wnc, ws)))
+        bytes_ifn[bits] = N * K * 2 + N * K * bits // 8 + N * K // 16
+        del wnc
 
     # practical HBM reference: a plain device-to-device copy of W's bf16 input
     # (reads and writes the same number of bytes), timed like the kernels
@@ -235,6 +242,11 @@ def main():
                            "GB/s": round(qw_b / (ms_rht * 1e-3) / 1e9, 1),
                            "frac_hbm_peak": round(qw_b / (ms_rht * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "frac_of_copy": round(qw_b / (ms_rht * 1e-3) / 1e9 / copy_gbs, 4)},
+        **{f"quantize_if{b}_W": {"ms": round(ms_ifn[b], 4), "bytes": bytes_ifn[b],
+                                  "GB/s": round(bytes_ifn[b] / (ms_ifn[b] * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(bytes_ifn[b] / (ms_ifn[b] * 1e-3) / 1e9
+                                                         / HBM_PEAK_GBS, 4)}
+           for b in (6, 3)},
         "hbm_copy_reference": {"bytes": copy_bytes, "GB/s": round(copy_gbs, 1),
                                "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
     }

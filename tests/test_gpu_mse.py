@@ -55,3 +55,17 @@ def test_rotation_makes_heavy_tails_prefer_int4():
     check(plain)
     check(rot)
     assert rot["int4_share"] > plain["int4_share"] + 0.1
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_ifn_error_not_above_either_fixed_format(bits):
+    """IF3 / IF6 keep the lower-error encoding per group, so their MSE is at
+    most that of the forced float and forced INT formats (the pages' claim
+    that the adaptive pattern holds across bit widths)."""
+    from adaptive_block_scaled_amd import mse_report
+    for t in (wl.c2_activations(rows=1024), wl.c3_rht_gradient(rows=1024)):
+        r = mse_report.report_tensor_ifn(t, bits)
+        print(r, flush=True)
+        assert r["mse_if"] <= r["mse_fp"] and r["mse_if"] <= r["mse_int"]
+        assert r["groups_if_above_best_fixed"] <= 2
+        assert 0.0 < r["int_share"] < 1.0
