@@ -237,8 +237,9 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
 // for its load).  One LDS-only barrier per slab, after which the eight W
 // fragments of the slab's first step are read before any MFMA is issued.
 // Within a slab, each MFMA step runs four sub-blocks of four MFMAs: (A block
-// 0, W blocks 0..3), (1, 0..3), (0, 4..7), (1, 4..7), so that each W
-// fragment's next-step read is issued two sub-blocks before its next use.
+// 0, W blocks 0..3), (1, 0..3), (0, 4..7), (1, 4..7); the eight W fragments
+// of the next step are read into a second register set at the start of the
+// step, a whole step before their use.
 // Each sub-block carries one code-word decode (about 16 VALU instructions):
 // A block 1's operand of step t-1 in sub-block 0 (for step 0, from a word
 // kept across the barrier), W words in sub-blocks 1 and 2, A block 0's
@@ -411,10 +412,10 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 
         // step 0's fragments first, all eight before any MFMA, so that only
         // the first read's latency is exposed after the barrier
-        half8 bv[8];
+        half8 bv[2][8];  // fragments of even / odd steps
 #pragma unroll
         for (int j = 0; j < 8; j++)
-            bv[j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
+            bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
         __builtin_amdgcn_sched_barrier(0);
         raw[P].load(acp, asp, wcp, wsp, sl, h, q, gpr);
 #pragma unroll
@@ -432,21 +433,22 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                 la0 = a_scale(raw[P], sw2_win, US2, sn + 1, 0, 0);
                 lw = w_scale(raw[P], sw2_win, US2, sn + 1, 0, 0);
             }
-            // sub-blocks: (A block 0, W 0..3), (1, 0..3), (0, 4..7), (1, 4..7):
-            // W fragments 0..3 are free after sub-block 1 and 4..7 after 3,
-            // two sub-blocks before the next step needs them
+            // the next step's eight fragments, a whole step ahead
+            if (t + 1 < kGroups) {
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    bv[(t + 1) & 1][j] = *reinterpret_cast<const half8*>(
+                        buf + w_off + j * FRAG_BLOCK + (t + 1) * FRAG_STEP);
+            }
+            // sub-blocks: (A block 0, W 0..3), (1, 0..3), (0, 4..7), (1, 4..7)
 #pragma unroll
             for (int sb = 0; sb < 4; sb++) {
                 const int i = sb & 1;  // A block of this sub-block's MFMAs
 #pragma unroll
                 for (int jj = 0; jj < 4; jj++) {
                     const int j = 4 * (sb >> 1) + jj;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][t], bv[j], acc[i][j],
-                                                                       0, 0, 0);
-                    // last use of fragment j in this step: fetch the next step's
-                    if (i == 1 && t + 1 < kGroups)
-                        bv[j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK +
-                                                                (t + 1) * FRAG_STEP);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][t], bv[t & 1][j],
+                                                                       acc[i][j], 0, 0, 0);
                 }
                 if (sb == 0) {
                     // t = 0: the word kept from the previous slab (sa1 holds its scale)
