@@ -19,7 +19,7 @@
 // One group per thread, one workgroup per 256 groups, the thread's loads
 // issued first.  Every rounding is decided by exact comparisons against
 // thresholds that are exact in fp32 (the grids' midpoints times the scale),
-// in binary searches with ties to the even index -- valid for any fp32 input.
+// ties to the even index -- valid for any fp32 input -- in branch-free code.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,9 +35,7 @@ struct Fmt;
 
 template <>
 struct Fmt<6> {
-    static constexpr int kFpLog2 = 5;      // 32 float magnitudes
-    static constexpr int kQLog2 = 5;       // INT magnitudes 0..31
-    static constexpr float kTop = 7.5f;
+    static constexpr float kTop = 7.5f;     // 32 float magnitudes, INT 0..31
     static constexpr float kDn = 15.0f, kDd = 62.0f;  // top / qmax = dn / dd
     // E2M3 magnitude of index i: 2 exponent bits (bias 1), 3 mantissa bits
     __device__ static float fp(int i) {
@@ -48,9 +46,7 @@ struct Fmt<6> {
 
 template <>
 struct Fmt<3> {
-    static constexpr int kFpLog2 = 2;      // E2M0: 0, 1, 2, 4
-    static constexpr int kQLog2 = 2;       // INT magnitudes 0..3
-    static constexpr float kTop = 4.0f;
+    static constexpr float kTop = 4.0f;     // E2M0: 0, 1, 2, 4; INT 0..3
     static constexpr float kDn = 4.0f, kDd = 3.0f;
     __device__ static float fp(int i) { return i == 0 ? 0.0f : __builtin_ldexpf(1.0f, i - 1); }
 };
@@ -59,26 +55,41 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
     return code >= 8u ? __uint_as_float((code + 960u) << 20) : (float)code * 0.001953125f;
 }
 
-// index of RNE(v / unit) on an ascending grid of 2^kLog2 values with
-// midpoints mid(k) (exact products unit * mid(k)); ties -> even index;
-// values past the last midpoint saturate
-template <int kLog2, typename Mid>
-__device__ __forceinline__ uint32_t rne_search(float v, Mid mid) {
-    uint32_t lo = 0;
-#pragma unroll
-    for (int step = 1 << (kLog2 - 1); step >= 1; step >>= 1) {
-        const uint32_t k = lo + step - 1;  // boundary between k and k + 1
-        const float t = mid(k);
-        const bool up = v > t || (v == t && (k & 1u));
-        lo = up ? k + 1 : lo;
-    }
-    return lo;
+// 1 if a magnitude ax (>= 0) rounds above the boundary t of index k (the
+// midpoint between grid values k and k + 1): ax > t, or ax == t for odd k,
+// so that ties go to the even index.  Non-negative floats order as their bit
+// patterns; a negative t is always passed and t = +inf never.
+__device__ __forceinline__ int passes(float ax, float t, int k) {
+    return (int)__float_as_uint(ax) + (k & 1) > (int)__float_as_uint(t) ? 1 : 0;
+}
+// the same for the INT boundary of |q| = k, given d = dd |x| - dn s (k + 1/2)
+// from one fma (its sign is exact and an exact zero is +0)
+__device__ __forceinline__ int passes_d(float d, int k) {
+    return (int)__float_as_uint(d) + (k & 1) > 0 ? 1 : 0;
 }
 
+// E2M3 magnitude of index k and the midpoint between k and k + 1, exactly:
+// with e = max(k >> 3, 1), (k + 8 - 8e) 2^(e - 4) and (2k + 17 - 16e) 2^(e - 5)
+__device__ __forceinline__ float e2m3_value(int k) {
+    const int e = k >> 3 > 1 ? k >> 3 : 1;
+    return __builtin_ldexpf((float)(k + 8 - 8 * e), e - 4);
+}
+__device__ __forceinline__ float e2m3_mid(int k) {
+    const int e = k >> 3 > 1 ? k >> 3 : 1;
+    return __builtin_ldexpf((float)(2 * k + 17 - 16 * e), e - 5);
+}
+
+// Every rounding below is "guess, then one exact comparison".  A guess
+// truncates an approximate quotient (at most a part in 2^21 off) to the grid
+// below it, which gives the correctly rounded index or the one below (the
+// grids are at least 2^-4 apart, relative); the comparison with the exact
+// fp32 threshold above the guess -- a product of at most 14 significant bits,
+// a normal number for the scales |E| <= 64 allows -- decides between them.
 template <int kBits, int kMode>
 __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp, float p_negexp,
                                                uint32_t (&out)[3], uint32_t& byte) {
     using F = Fmt<kBits>;
+    constexpr float kInf = __builtin_inff();
     float a = 0.0f;
     bool finite = true;
 #pragma unroll
@@ -92,59 +103,84 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
         byte = 0x7Fu;
         return;
     }
-    // scale code: RNE_E4M3(a 2^-E / top) over the 127 finite codes: a' vs
-    // top * (v_k + v_{k+1}) / 2, exact (4 + 5 bits); 7 binary-search steps
-    // over the 126 midpoints (the 128th boundary is never reached)
+    // scale code RNE_E4M3(a 2^-E / top) over the 127 finite codes; the
+    // boundary above code k is top (v_k + v_{k+1}) / 2 (4 + 5 bits, exact)
     const float ap = a * p_negexp;
-    uint32_t sc = 0;
-#pragma unroll
-    for (int step = 64; step >= 1; step >>= 1) {
-        const uint32_t k = sc + step - 1;
-        if (k < 126u) {
-            const float t = F::kTop * (0.5f * (e4m3_value(k) + e4m3_value(k + 1)));
-            const bool up = ap > t || (ap == t && (k & 1u));
-            sc = up ? k + 1 : sc;
-        }
-    }
+    const float qg = ap * (1.0f / F::kTop);
+    int sc = qg < 0.015625f ? (int)(qg * 512.0f) : (int)(__float_as_uint(qg) >> 20) - 960;
+    sc = sc < 126 ? sc : 126;
+    sc += passes(ap, sc < 126 ? F::kTop * (0.5f * (e4m3_value(sc) + e4m3_value(sc + 1))) : kInf,
+                 sc);
     if (sc == 0) {
         byte = 0;
         return;
     }
-    const float s = e4m3_value(sc) * p_exp;
+    const float s = e4m3_value((uint32_t)sc) * p_exp;
     const float sdd = F::kDd * s, sdn = F::kDn * s;
+    constexpr int kFMax = (1 << (kBits - 1)) - 1, kQMax = kFMax;
+    // IF6: reciprocals for the guesses.  IF3: its three boundaries of each
+    // kind, counted directly.
+    const float r = __builtin_amdgcn_rcpf(s);
+    const float rq = r * (F::kDd / F::kDn);
+    float tf[3], tq[3];
+    if constexpr (kBits == 3) {
+#pragma unroll
+        for (int k = 0; k < 3; k++) {
+            tf[k] = s * (0.5f * (F::fp(k) + F::fp(k + 1)));
+            tq[k] = sdn * ((float)k + 0.5f);
+        }
+    }
     float ef = 0.0f, ei = 0.0f;
-    uint32_t cf[16], ci[16];
+    // magnitude fields of both candidates and the sign field, kBits per element
+    uint32_t mf[3] = {0, 0, 0}, mq[3] = {0, 0, 0}, sg[3] = {0, 0, 0};
+    auto put = [](uint32_t(&f)[3], uint32_t c, int bit) {
+        f[bit >> 5] |= c << (bit & 31);
+        if ((bit & 31) + kBits > 32) f[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+    };
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const float ax = __builtin_fabsf(v[i]);
-        const uint32_t fi = rne_search<F::kFpLog2>(
-            ax, [&](uint32_t k) { return s * (0.5f * (F::fp(k) + F::fp(k + 1))); });
-        // INT: |q| > k  <=>  dd |x| > dn s (k + 1/2); the sign of the fma is exact
-        uint32_t q = 0;
+        int fi, q;
+        float fvs;  // the float candidate's value times dd s, exact (at most 14 bits)
+        if constexpr (kBits == 6) {
+            // guess: 8u below 1 (step 1/8), else 8 e + the top three
+            // mantissa bits; min/max instead of a select keep it branch-free
+            // (at the top, the boundary below index 31 stands in and the
+            // result is clamped)
+            const float u = ax * r;
+            const int g = min((int)(__builtin_fminf(u, 1.0f) * 8.0f) +
+                                  (int)(__float_as_uint(__builtin_fmaxf(u, 1.0f)) >> 20) - 1016,
+                              kFMax);
+            // with e = max(gm >> 3, 1), the midpoint above gm is nm 2^(e-5)
+            // and the magnitudes on either side are (nm -+ 1) 2^(e-5)
+            const int gm = min(g, kFMax - 1);
+            const int e = max(gm >> 3, 1);
+            const int nm = 2 * gm + 17 - 16 * e;
+            fi = min(g + passes(ax, (float)nm * __builtin_ldexpf(s, e - 5), g), kFMax);
+            fvs = (float)(nm - 1 + 2 * (fi - gm)) * __builtin_ldexpf(sdd, e - 5);
+            // INT: |q| > k  <=>  dd |x| > dn s (k + 1/2)
+            const int h = (int)__builtin_fminf(ax * rq, (float)kQMax);
+            const float kh = (float)min(h, kQMax - 1) + 0.5f;
+            q = min(h + passes_d(__builtin_fmaf(ax, F::kDd, -(sdn * kh)), h), kQMax);
+        } else {
+            fi = passes(ax, tf[0], 0) + passes(ax, tf[1], 1) + passes(ax, tf[2], 2);
+            fvs = (float)((1 << fi) >> 1) * sdd;
+            q = 0;
 #pragma unroll
-        for (int step = 1 << (F::kQLog2 - 1); step >= 1; step >>= 1) {
-            const uint32_t k = q + step - 1;
-            const float d = __builtin_fmaf(ax, F::kDd, -sdn * ((float)k + 0.5f));
-            const bool up = d > 0.0f || (d == 0.0f && (k & 1u));
-            q = up ? k + 1 : q;
+            for (int k = 0; k < 3; k++) q += passes_d(__builtin_fmaf(ax, F::kDd, -tq[k]), k);
         }
-        const float df = __builtin_fmaf(ax, F::kDd, -(F::fp(fi) * sdd));
+        const float df = __builtin_fmaf(ax, F::kDd, -fvs);
         const float di = __builtin_fmaf(ax, F::kDd, -((float)q * sdn));
         ef = __builtin_fmaf(df, df, ef);
         ei = __builtin_fmaf(di, di, ei);
-        const uint32_t sg = (__float_as_uint(v[i]) >> 31) << (kBits - 1);
-        cf[i] = sg | fi;
-        ci[i] = sg | q;
+        put(mf, (uint32_t)fi, kBits * i);
+        put(mq, (uint32_t)q, kBits * i);
+        put(sg, (__float_as_uint(v[i]) >> 31) << (kBits - 1), kBits * i);
     }
     const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const uint32_t c = use_int ? ci[i] : cf[i];
-        const int bit = kBits * i;
-        out[bit >> 5] |= c << (bit & 31);
-        if ((bit & 31) + kBits > 32) out[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-    }
-    byte = sc | (use_int ? 0x80u : 0u);
+    for (int w = 0; w < 3; w++) out[w] = (use_int ? mq[w] : mf[w]) | sg[w];
+    byte = (uint32_t)sc | (use_int ? 0x80u : 0u);
 }
 
 template <int kBits, int kMode, bool kBf16>

@@ -122,6 +122,41 @@ def test_edge_groups_and_strided_input(oracle_mod, bits):
 
 
 @pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("e", [0, -40, 40, -64, 64])
+def test_ties_and_near_ties(oracle_mod, bits, e):
+    """fp32 values at and next to every rounding boundary of both grids, in
+    groups whose first element (top * s') pins the scale: exercises the
+    rounding decisions themselves (ties to the even index, saturation)."""
+    top, qmax = (7.5, 31) if bits == 6 else (4.0, 3)
+    fp = sorted({float(v) for v in oracle_mod_grid(oracle_mod, bits)})
+    vals = []
+    for sc in (0x08, 0x23, 0x38, 0x3B, 0x55, 0x7E):
+        s = (1 + (sc & 7) / 8) * 2.0 ** ((sc >> 3) - 7) * 2.0 ** e
+        bounds = [(fp[k] + fp[k + 1]) / 2 * s for k in range(len(fp) - 1)]
+        bounds += [(k + 0.5) * top / qmax * s for k in range(qmax)]
+        cand = []
+        for b in bounds:
+            b32 = np.float32(b)
+            cand += [b32, np.nextafter(b32, np.float32(0)), np.nextafter(b32, np.float32(np.inf))]
+        cand = np.array(cand, np.float32)
+        cand[1::2] *= -1
+        for i in range(0, len(cand), 15):
+            chunk = cand[i:i + 15]
+            g = np.zeros(16, np.float32)
+            g[0] = np.float32(top * s)
+            g[1:1 + len(chunk)] = chunk
+            vals.append(g)
+    x = np.stack(vals).reshape(-1, 64) if len(vals) % 4 == 0 else np.stack(vals).reshape(1, -1)
+    c, s_ = check_q(oracle_mod, x, bits, "f32", e, label="ties")
+    check_dq(oracle_mod, c, s_, bits, e)
+    assert (s_.cpu().numpy() & 0x7F).min() > 0
+
+
+def oracle_mod_grid(oracle_mod, bits):
+    return [oracle_mod.ifn_fp_value(bits, i) for i in range(1 << (bits - 1))]
+
+
+@pytest.mark.parametrize("bits", [3, 6])
 def test_dequantize_every_code(oracle_mod, bits):
     # every code under both flags and a spread of scale bytes (NaN scale included)
     nm = 1 << bits
