@@ -416,7 +416,6 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 #pragma unroll
         for (int j = 0; j < 8; j++)
             bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
-        __builtin_amdgcn_sched_barrier(0);
         raw[P].load(acp, asp, wcp, wsp, sl, h, q, gpr);
 #pragma unroll
         for (int t = 0; t < kGroups; t++) {
@@ -459,18 +458,17 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                 } else {
                     w_store(x, sw, k, gg, sb == 1 ? 0 : 1, nbuf);
                 }
-                // the slab's first sub-block starts with its decode (registers
-                // only), which covers the wait for the first fragment
-                if (t == 0 && sb == 0) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+                // interleave: each MFMA followed by five VALU and up to two
+                // LDS reads; no fence between sub-blocks, so the scheduler
+                // may pull a later sub-block's independent work forward
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
                     if (m == 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
                     if (m == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
         w13 = x.aword(1, kGroups - 1);
