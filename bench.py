@@ -10,13 +10,15 @@ timed region.  `value` is the step's throughput counted as the GEMM's
 2*M*N*K flops per step time (TFLOP/s); per-kernel figures (quantize GB/s
 against the 8 TB/s HBM peak, GEMM TFLOP/s against the 2.5 PFLOP/s dense
 fp16 MFMA peak) are in `kernels`, and `roofline` reports the dominant
-kernel.  After the step loop, three more kernels are timed on W's 470 MB,
+kernel.  After the step loop, five more kernels are timed on W's 470 MB,
 beyond the 256 MB last-level cache, and reported in `kernels` only: the
 dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0),
 the quantize after a random-sign 16-point Hadamard rotation of each group,
-and the IF6 and IF3 quantizes.  `kernels` also holds a plain device-to-device copy of W's input,
-timed the same way, as the practical HBM reference for the memory-bound
-kernels (`frac_of_copy`).
+and the IF6 and IF3 quantizes.  `kernels` also holds two practical
+references timed the same way: a plain device-to-device copy of W's input
+for the memory-bound kernels (`frac_of_copy`), and the vendor library's
+dense fp16 GEMM of the same shape with fp32 output (torch.mm, no IF4
+decode) for the GEMM (`frac_of_fp16_library_gemm`).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -205,6 +207,15 @@ def main():
     copy_gbs = copy_bytes / (ev_c[0].elapsed_time(ev_c[1]) / nd * 1e-3) / 1e9
     del Wc
 
+    # practical MFMA reference: the vendor library's dense fp16 GEMM of the
+    # same shape and fp32 output (torch.mm -> hipBLASLt), no IF4 decode; the
+    # chip is power-limited, so this is what its matrix cores sustain here
+    a16 = torch.empty((M, K), dtype=torch.float16, device=dev).normal_()
+    w16 = torch.empty((N, K), dtype=torch.float16, device=dev).normal_()
+    ms_ref = time_launches(lambda: torch.mm(a16, w16.t(), out_dtype=torch.float32))
+    del a16, w16
+    ref_tflops = 2.0 * M * N * K / (ms_ref * 1e-3) / 1e12
+
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -229,7 +240,8 @@ def main():
                         "frac_hbm_peak": round(qa_gbs / HBM_PEAK_GBS, 4),
                         "frac_of_copy": round(qa_gbs / copy_gbs, 4)},
         "gemm": {"ms": round(ms_gemm, 4), "flop": flops, "TFLOP/s": round(gemm_tflops, 1),
-                 "frac_mfma_peak": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
+                 "frac_mfma_peak": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                 "frac_of_fp16_library_gemm": round(gemm_tflops / ref_tflops, 4)},
         "dequantize_W_bf16": {"ms": round(ms_deq, 4), "bytes": dequant_bytes(N, K),
                               "GB/s": round(deq_gbs, 1),
                               "frac_hbm_peak": round(deq_gbs / HBM_PEAK_GBS, 4),
@@ -249,6 +261,8 @@ def main():
            for b in (6, 3)},
         "hbm_copy_reference": {"bytes": copy_bytes, "GB/s": round(copy_gbs, 1),
                                "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
+        "fp16_library_gemm_reference": {"ms": round(ms_ref, 4), "TFLOP/s": round(ref_tflops, 1),
+                                        "frac_mfma_peak": round(ref_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
     }
     roofline = {"kernel": "gemm", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
