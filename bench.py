@@ -10,8 +10,9 @@ timed region.  `value` is the step's throughput counted as the GEMM's
 2*M*N*K flops per step time (TFLOP/s); per-kernel figures (quantize GB/s
 against the 8 TB/s HBM peak, GEMM TFLOP/s against the 2.5 PFLOP/s dense
 fp16 MFMA peak) are in `kernels`, and `roofline` reports the dominant
-kernel.  After the step loop, five more kernels are timed on W's 470 MB,
-beyond the 256 MB last-level cache, and reported in `kernels` only: the
+kernel.  After the step loop, more kernels are timed on W's 470 MB, beyond
+the 256 MB last-level cache, and reported in `kernels` only: the W quantize
+again, back to back on its own, the
 dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0),
 the quantize after a random-sign 16-point Hadamard rotation of each group,
 and the IF6 and IF3 quantizes.  `kernels` also holds two practical
@@ -178,6 +179,9 @@ def main():
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / n
 
+    # the W quantize again, back to back on its own (in the step it follows
+    # the GEMM, whose 940 MB of output is still being written back)
+    ms_qw_alone = time_launches(lambda: if4.quantize(W, ew, out=(wc, ws)))
     wtc = torch.empty((K, N // 2), dtype=torch.uint8, device=dev)
     wts = torch.empty((K, N // 16), dtype=torch.uint8, device=dev)
     ms_qt = time_launches(lambda: if4.quantize_t(W, ew, out=(wtc, wts)))
@@ -236,6 +240,12 @@ def main():
         "quantize_W": {"ms": round(ms_qw, 4), "bytes": qw_b, "GB/s": round(qw_gbs, 1),
                         "frac_hbm_peak": round(qw_gbs / HBM_PEAK_GBS, 4),
                         "frac_of_copy": round(qw_gbs / copy_gbs, 4)},
+        "quantize_W_back_to_back": {"ms": round(ms_qw_alone, 4), "bytes": qw_b,
+                                    "GB/s": round(qw_b / (ms_qw_alone * 1e-3) / 1e9, 1),
+                                    "frac_hbm_peak": round(qw_b / (ms_qw_alone * 1e-3) / 1e9
+                                                           / HBM_PEAK_GBS, 4),
+                                    "frac_of_copy": round(qw_b / (ms_qw_alone * 1e-3) / 1e9
+                                                          / copy_gbs, 4)},
         "quantize_A": {"ms": round(ms_qa, 4), "bytes": qa_b, "GB/s": round(qa_gbs, 1),
                         "frac_hbm_peak": round(qa_gbs / HBM_PEAK_GBS, 4),
                         "frac_of_copy": round(qa_gbs / copy_gbs, 4)},
