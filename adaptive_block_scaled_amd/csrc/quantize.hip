@@ -12,8 +12,8 @@
 // error sums, the selection and the nibble packing happen in that lane's
 // registers with no cross-lane traffic.  A wave reads 64 consecutive groups
 // (2 KB of bf16) and writes 512 B of codes and 64 B of scales, all
-// contiguous.  The bf16 kernel is one-shot (two groups per thread, all
-// loads issued first); the exact fp32 kernel is a grid-stride loop.
+// contiguous.  The bf16 kernel is one-shot (one group per thread, its loads
+// issued first); the exact fp32 kernel is a grid-stride loop.
 //
 // Every rounding decision is taken exactly, for any fp32 input: each code
 // is the count of grid midpoints the value passes, compared against exactly
@@ -358,11 +358,13 @@ __device__ __forceinline__ void fast_group(const float (&v)[16], const float2* r
 // apart (a wave's loads stay contiguous: 64 lanes x 32 bytes), with all of its
 // loads issued before the first group is quantized, and one workgroup per
 // kThreads * kGPT groups.  Past the end a load re-reads the last group and
-// its store is skipped, so no load sits behind a branch.  (A grid-stride loop
-// over fewer workgroups, with the next group prefetched into a second
-// register set, measured 8-11% slower: it keeps one group's loads in flight
-// per thread instead of kGPT.)
-constexpr int kGPT = 2;
+// its store is skipped, so no load sits behind a branch.  One group per
+// thread: on the 470 MB weight one, two and four groups per thread run alike,
+// and on 86-172 MB tensors one is 4-9% faster (more, smaller workgroups fill
+// the chip sooner and leave a shorter tail).  (A grid-stride loop over fewer
+// workgroups, with the next group prefetched into a second register set,
+// measured 8-11% slower on the weight.)
+constexpr int kGPT = 1;
 
 template <int kMode, bool kContig, bool kRotate>
 __global__ void __launch_bounds__(kThreads)

@@ -15,7 +15,9 @@ the 256 MB last-level cache, and reported in `kernels` only: the W quantize
 again, back to back on its own, the
 dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0),
 the quantize after a random-sign 16-point Hadamard rotation of each group,
-and the IF6 and IF3 quantizes.  `kernels` also holds two practical
+and the IF6 and IF3 quantizes.  `configs` times the smaller workloads at
+their own shapes (C2 and C3 quantizes, C4 GEMM), each cycling through
+enough buffer sets to stream from HBM.  `kernels` also holds two practical
 references timed the same way: a plain device-to-device copy of W's input
 for the memory-bound kernels (`frac_of_copy`), and the vendor library's
 dense fp16 GEMM of the same shape with fp32 output (torch.mm, no IF4
@@ -279,6 +281,11 @@ def main():
                 "frac": round(gemm_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(GEMM_HBM_PROFILE, GEMM_SOURCE)}
 
+    del Y
+    t0 = time.time()
+    configs = time_other_configs(torch, if4, wl, dev)
+    log(f"timed the C2, C3 and C4 workloads in {time.time() - t0:.1f}s")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(a_host, w_host, ea, ew, M, N, K, args.cpu_budget_s)
@@ -304,10 +311,86 @@ def main():
             "parallelism": "single-gpu",
         },
         "kernels": kernels,
+        "configs": configs,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def mean_launch_ms(torch, calls, n=100, warmup=200, batches=3):
+    """Time per launch: the median over `batches` of the mean of n
+    back-to-back launches between one pair of HIP events, cycling through
+    `calls` (one per buffer set, so that consecutive launches touch different
+    memory).  The long warm-up lets the clock settle after the heavier work
+    timed before."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    per = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / n)
+    return sorted(per)[batches // 2]
+
+
+def time_other_configs(torch, if4, wl, dev, min_bytes=512 << 20):
+    """The smaller workloads at their own shapes: the C2 activation and C3
+    gradient quantizes (C3 also through the fused rotate-and-quantize from
+    its raw gradient) and the C4 GEMM.  Their working sets fit the 256 MB
+    last-level cache, so each cycles through enough input and output sets to
+    exceed 512 MB and every launch streams from HBM."""
+    out = {}
+
+    def quant_sets(x_host, e, rht_mask=None):
+        R, C = x_host.shape
+        byts = R * C * 2 + R * C // 2 + R * C // 16
+        nset = -(-min_bytes // byts)
+        src = torch.from_numpy(x_host).to(torch.bfloat16).to(dev)
+        xs = [src] + [src.clone() for _ in range(nset - 1)]
+        cs = [(torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
+               torch.empty((R, C // 16), dtype=torch.uint8, device=dev)) for _ in range(nset)]
+        if rht_mask is None:
+            calls = [lambda x=x, o=o: if4.quantize(x, e, out=o) for x, o in zip(xs, cs)]
+        else:
+            calls = [lambda x=x, o=o: if4.quantize_rht(x, rht_mask, e, out=o) for x, o in zip(xs, cs)]
+        ms = mean_launch_ms(torch, calls)
+        del xs, cs
+        gbs = byts / (ms * 1e-3) / 1e9
+        return {"shape": [R, C], "E": e, "buffer_sets": nset, "ms": round(ms, 5), "bytes": byts,
+                "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    t = wl.c2_activations()
+    out["C2_quantize"] = quant_sets(t.values, t.scale_exp)
+    t = wl.c3_rht_gradient()
+    e3 = t.scale_exp
+    out["C3_quantize"] = quant_sets(t.values, e3)
+    # the same gradient before its rotation (same draws), rotated inside the
+    # quantize, at the rotated tensor's exponent
+    t, mask = wl.c3_raw_gradient()
+    out["C3_rotate_quantize"] = quant_sets(t.values, e3, rht_mask=mask)
+    del t
+
+    a_t, w_t = wl.c4_gemm()
+    m, k = a_t.values.shape
+    n = w_t.values.shape[0]
+    ea, ew = a_t.scale_exp, w_t.scale_exp
+    ac, as_ = if4.quantize(torch.from_numpy(a_t.values).to(torch.bfloat16).to(dev), ea)
+    wc, ws = if4.quantize(torch.from_numpy(w_t.values).to(torch.bfloat16).to(dev), ew)
+    nset = -(-min_bytes // (m * n * 4))
+    cs = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(nset)]
+    calls = [lambda c=c: if4.gemm(ac, as_, ea, wc, ws, ew, out=c) for c in cs]
+    ms = mean_launch_ms(torch, calls)
+    del cs
+    tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    out["C4_gemm"] = {"shape": [m, n, k], "buffer_sets": nset, "ms": round(ms, 5),
+                      "flop": 2 * m * n * k, "TFLOP/s": round(tf, 1),
+                      "frac_mfma_peak": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+    return out
 
 
 def cpu_baseline(a_host, w_host, ea, ew, M, N, K, budget_s):
