@@ -407,6 +407,12 @@ def cpu_baseline(a_host, w_host, ea, ew, M, N, K, budget_s):
     t = time.perf_counter()
     ac, as_ = oracle.quantize(a_host[:ra], ea, nthreads=nthreads)
     t_qa = (time.perf_counter() - t) * (M / ra)
+    # the quantize on one core too (a smaller row sample)
+    r1 = 256
+    t = time.perf_counter()
+    oracle.quantize(w_host[:r1], ew, nthreads=1)
+    t_qw1 = (time.perf_counter() - t) * (N / r1)
+    qw_bytes = N * K * 2 + N * K // 2 + N * K // 16
     # GEMM: probe one output row on 1024 columns, then size the row sample
     cols = np.arange(rw, dtype=np.int64)
     t = time.perf_counter()
@@ -423,9 +429,12 @@ def cpu_baseline(a_host, w_host, ea, ew, M, N, K, budget_s):
         "unit": "TFLOP/s",
         "cores": nthreads,
         "kind": "oracle",
+        "quantize_W_GB/s": round(qw_bytes / t_qw / 1e9, 3),
+        "quantize_W_GB/s_1core": round(qw_bytes / t_qw1 / 1e9, 3),
         "sample": (f"oracle quantize of {rw} W rows and {ra} A rows, fp64 GEMM oracle on "
                    f"{n_rows} rows x {rw} cols; each part scaled to full size "
-                   f"(quantize W {t_qw:.1f}s, A {t_qa:.1f}s, GEMM {t_g:.0f}s per step)"),
+                   f"(quantize W {t_qw:.1f}s, A {t_qa:.1f}s, GEMM {t_g:.0f}s per step); the W "
+                   f"quantize also on one core, {r1} rows scaled ({t_qw1:.1f}s)"),
     }
 
 
