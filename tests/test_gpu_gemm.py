@@ -100,6 +100,29 @@ def test_nan_scale_propagates(oracle_mod):
     assert np.isfinite(np.delete(got, 5, axis=0)).all()
 
 
+@pytest.mark.parametrize("mnk", [(5965, 4040, 512), (4452, 4645, 768), (2560, 7000, 1024)])
+def test_more_tiles_than_compute_units(oracle_mod, mnk):
+    """Shapes with more 256x256 tiles than the chip has compute units (384,
+    342 and 280 tiles), ragged in M and N: the workgroups each run several
+    tiles in turn, some more than others.  One row in every M-tile (and the
+    last row) is checked against all N columns, so every tile is covered."""
+    M, N, K = mnk
+    print(f"[gemm] multi-tile M={M} N={N} K={K}", flush=True)
+    ac, as_, ea, wc, ws, ew = quantized_pair(oracle_mod, M, N, K, 11 + K)
+    got = gpu_gemm(ac, as_, ea, wc, ws, ew)
+    tiles_m = (M + 255) // 256
+    rows = sorted({min(M - 1, t * 256 + (t * 37) % 256) for t in range(tiles_m)} | {M - 1, 0})
+    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew, rows=np.array(rows))
+    err = rel_fro(got[rows], ref)
+    print(f"    rel fro on {len(rows)} rows x {N} cols: {err:.3e}", flush=True)
+    assert err <= TOL
+    # every tile individually: each sampled row's 256-column blocks
+    g, r_ = got[rows].astype(np.float64), ref
+    for j in range(0, N, 256):
+        blk = np.linalg.norm(g[:, j:j + 256] - r_[:, j:j + 256]) / np.linalg.norm(r_[:, j:j + 256])
+        assert blk <= 4 * TOL, (j, blk)
+
+
 def test_c4_full_size(oracle_mod):
     a, w = wl.c4_gemm()
     ea, ew = a.scale_exp, w.scale_exp
