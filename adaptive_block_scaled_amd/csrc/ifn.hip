@@ -122,6 +122,7 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
     // kind, counted directly.
     const float r = __builtin_amdgcn_rcpf(s);
     const float rq = r * (F::kDd / F::kDn);
+    const float sdn_half = 0.5f * sdn;
     float tf[3], tq[3];
     if constexpr (kBits == 3) {
 #pragma unroll
@@ -144,24 +145,24 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
         float fvs;  // the float candidate's value times dd s, exact (at most 14 bits)
         if constexpr (kBits == 6) {
             // guess: 8u below 1 (step 1/8), else 8 e + the top three
-            // mantissa bits; min/max instead of a select keep it branch-free
-            // (at the top, the boundary below index 31 stands in and the
-            // result is clamped)
+            // mantissa bits (min/max instead of a select keep it
+            // branch-free), clamped to 30 so that the boundary above it
+            // exists; a guess is never above the correctly rounded index
             const float u = ax * r;
             const int g = min((int)(__builtin_fminf(u, 1.0f) * 8.0f) +
                                   (int)(__float_as_uint(__builtin_fmaxf(u, 1.0f)) >> 20) - 1016,
-                              kFMax);
-            // with e = max(gm >> 3, 1), the midpoint above gm is nm 2^(e-5)
+                              kFMax - 1);
+            // with e = max(g >> 3, 1), the midpoint above g is nm 2^(e-5)
             // and the magnitudes on either side are (nm -+ 1) 2^(e-5)
-            const int gm = min(g, kFMax - 1);
-            const int e = max(gm >> 3, 1);
-            const int nm = 2 * gm + 17 - 16 * e;
-            fi = min(g + passes(ax, (float)nm * __builtin_ldexpf(s, e - 5), g), kFMax);
-            fvs = (float)(nm - 1 + 2 * (fi - gm)) * __builtin_ldexpf(sdd, e - 5);
-            // INT: |q| > k  <=>  dd |x| > dn s (k + 1/2)
-            const int h = (int)__builtin_fminf(ax * rq, (float)kQMax);
-            const float kh = (float)min(h, kQMax - 1) + 0.5f;
-            q = min(h + passes_d(__builtin_fmaf(ax, F::kDd, -(sdn * kh)), h), kQMax);
+            const int e = max(g >> 3, 1);
+            const int nm = 2 * g + 17 - 16 * e;
+            const int up = passes(ax, (float)nm * __builtin_ldexpf(s, e - 5), g);
+            fi = g + up;
+            fvs = (float)(nm - 1 + 2 * up) * __builtin_ldexpf(sdd, e - 5);
+            // INT: |q| > k  <=>  dd |x| > dn s (k + 1/2), the threshold
+            // dn s k + dn s / 2 exact in one fma
+            const int h = (int)__builtin_fminf(ax * rq, (float)(kQMax - 1));
+            q = h + passes_d(__builtin_fmaf(ax, F::kDd, -__builtin_fmaf((float)h, sdn, sdn_half)), h);
         } else {
             fi = passes(ax, tf[0], 0) + passes(ax, tf[1], 1) + passes(ax, tf[2], 2);
             fvs = (float)((1 << fi) >> 1) * sdd;
