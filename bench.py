@@ -424,10 +424,20 @@ def cpu_baseline(a_host, w_host, ea, ew, M, N, K, budget_s):
                            nthreads=nthreads)
     t_g = (time.perf_counter() - t) * (M / n_rows) * (N / rw)
     total = t_qw + t_qa + t_g
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(2.0 * M * N * K / total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": nthreads,
+        "cpu": cpu_model,
         "kind": "oracle",
         "quantize_W_GB/s": round(qw_bytes / t_qw / 1e9, 3),
         "quantize_W_GB/s_1core": round(qw_bytes / t_qw1 / 1e9, 3),
