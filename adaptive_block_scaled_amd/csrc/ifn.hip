@@ -237,11 +237,27 @@ quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64
 // dn s'/dd rounded toward zero and l = fl32((dn s' - dd h) * fl32(1/dd)) --
 // correctly rounded for every E4M3 s' and |q| (checked exhaustively in exact
 // arithmetic), with l >= 0 so that a zero magnitude keeps its sign.
+//
+// Both forms are one fma: every element is fma(A, HE, A * LE) with A the
+// code's signed integer on its grid and (HE, LE) a per-scale-byte pair --
+// INT: A = +-|q|, (HE, LE) = (h, l) 2^E; FP: A = +-fp(idx) * kFpDen (an
+// integer), (HE, LE) = (s' 2^E / kFpDen, 0), whose product is exact.  Each
+// workgroup tabulates A for the 2 x 2^bits (flag, code) pairs and (HE, LE)
+// for the 256 scale bytes in LDS while its loads are in flight, so an element
+// costs one LDS read, a multiply and an fma.  (A NaN scale byte gives NaN.)
+template <int kBits>
+struct Fp {
+    static constexpr float kDen = kBits == 6 ? 8.0f : 1.0f;  // fp(idx) * kDen is an integer
+};
+
 template <int kBits, bool kBf16>
 __global__ void __launch_bounds__(kThreads)
 dequantize_ifn_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       int64_t rows, int64_t gpr, void* __restrict__ y, int64_t ld_y, float p_exp) {
     using F = Fmt<kBits>;
+    constexpr int kCodes = 1 << kBits;
+    __shared__ float2 stab[256];
+    __shared__ float ctab[2 * kCodes];
     const int64_t ngroups = rows * gpr;
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t g = gid < ngroups - 1 ? gid : ngroups - 1;
@@ -258,16 +274,35 @@ dequantize_ifn_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
         w[2] = 0;
     }
     const uint32_t b = scales[g];
-    const float sp = (b & 0x7Fu) == 0x7Fu ? __uint_as_float(0x7FC00000u) : e4m3_value(b & 0x7Fu);
-    const bool is_int = (b & 0x80u) != 0;
-    float h, l;
+
+    // the tables, while the loads are in flight
     {
-        const float num = F::kDn * sp;  // exact
-        h = num / F::kDd;
-        if (__builtin_fmaf(-h, F::kDd, num) < 0.0f) h = __uint_as_float(__float_as_uint(h) - 1u);
-        l = __builtin_fmaf(-h, F::kDd, num) * (1.0f / F::kDd);
+        const uint32_t t = threadIdx.x;  // scale byte t
+        const float sp =
+            (t & 0x7Fu) == 0x7Fu ? __uint_as_float(0x7FC00000u) : e4m3_value(t & 0x7Fu);
+        float2 e;
+        if (t & 0x80u) {
+            const float num = F::kDn * sp;  // exact
+            float h = num / F::kDd;
+            if (__builtin_fmaf(-h, F::kDd, num) < 0.0f) h = __uint_as_float(__float_as_uint(h) - 1u);
+            const float l = __builtin_fmaf(-h, F::kDd, num) * (1.0f / F::kDd);
+            e = make_float2(h * p_exp, l * p_exp);
+        } else {
+            e = make_float2(sp * p_exp * (1.0f / Fp<kBits>::kDen), 0.0f);
+        }
+        stab[t] = e;
+        if (t < 2u * kCodes) {  // (flag, code) -> signed integer grid value
+            const uint32_t c = t & (kCodes - 1u), mag = c & (kCodes / 2 - 1u);
+            const float a = (t >= (uint32_t)kCodes) ? (float)mag : F::fp((int)mag) * Fp<kBits>::kDen;
+            ctab[t] = (c >> (kBits - 1)) ? -a : a;
+        }
     }
-    const float he = h * p_exp, le = l * p_exp, se = sp * p_exp;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    const float2 e = stab[b];
+    const uint32_t fbase = (b >> 7) << kBits;  // INT codes in the table's upper half
     float out[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
@@ -275,10 +310,8 @@ dequantize_ifn_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
         uint32_t c = w[bit >> 5] >> (bit & 31);
         if ((bit & 31) + kBits > 32) c |= w[(bit >> 5) + 1] << (32 - (bit & 31));
         c &= (1u << kBits) - 1u;
-        const uint32_t mag = c & ((1u << (kBits - 1)) - 1u);
-        const float m = (float)mag;
-        const float val = is_int ? __builtin_fmaf(m, he, m * le) : F::fp((int)mag) * se;
-        out[i] = (c >> (kBits - 1)) ? -val : val;
+        const float a = ctab[fbase + c];
+        out[i] = __builtin_fmaf(a, e.x, a * e.y);
     }
     if (gid >= ngroups) return;
     const int64_t r = gid / gpr;

@@ -15,7 +15,7 @@ the 256 MB last-level cache, and reported in `kernels` only: the W quantize
 again, back to back on its own, the
 dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0),
 the quantize after a random-sign 16-point Hadamard rotation of each group,
-and the IF6 and IF3 quantizes.  `configs` times the smaller workloads at
+and the IF6 and IF3 quantizes and dequantizes.  `configs` times the smaller workloads at
 their own shapes (C2 and C3 quantizes, C4 GEMM), each cycling through
 enough buffer sets to stream from HBM.  `kernels` also holds two practical
 references timed the same way: a plain device-to-device copy of W's input
@@ -191,12 +191,17 @@ def main():
     mask = wl.sign_mask(wl.random_signs(np.random.default_rng(0)))
     ms_rht = time_launches(lambda: if4.quantize_rht(W, mask, ew + 2, out=(wc, ws)))
     # IF6 and IF3 (3 and 6 bits per value) of the same weight
-    ms_ifn, bytes_ifn = {}, {}
+    # (quantize, then the dequantize of those codes back to bf16)
+    ms_ifn, bytes_ifn, ms_difn = {}, {}, {}
+    Yn = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     for bits in (6, 3):
         wnc = torch.empty((N, K // 16 * 2 * bits), dtype=torch.uint8, device=dev)
         ms_ifn[bits] = time_launches(lambda: if4.quantize_ifn(W, bits, ew, out=(wnc, ws)))
         bytes_ifn[bits] = N * K * 2 + N * K * bits // 8 + N * K // 16
+        ms_difn[bits] = time_launches(
+            lambda: if4.dequantize_ifn(wnc, ws, bits, ew, torch.bfloat16, out=Yn))
         del wnc
+    del Yn
 
     # practical HBM reference: a plain device-to-device copy of W's bf16 input
     # (reads and writes the same number of bytes), timed like the kernels
@@ -270,6 +275,11 @@ def main():
                                   "GB/s": round(bytes_ifn[b] / (ms_ifn[b] * 1e-3) / 1e9, 1),
                                   "frac_hbm_peak": round(bytes_ifn[b] / (ms_ifn[b] * 1e-3) / 1e9
                                                          / HBM_PEAK_GBS, 4)}
+           for b in (6, 3)},
+        **{f"dequantize_if{b}_W_bf16": {"ms": round(ms_difn[b], 4), "bytes": bytes_ifn[b],
+                                         "GB/s": round(bytes_ifn[b] / (ms_difn[b] * 1e-3) / 1e9, 1),
+                                         "frac_hbm_peak": round(bytes_ifn[b] / (ms_difn[b] * 1e-3)
+                                                                / 1e9 / HBM_PEAK_GBS, 4)}
            for b in (6, 3)},
         "hbm_copy_reference": {"bytes": copy_bytes, "GB/s": round(copy_gbs, 1),
                                "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
