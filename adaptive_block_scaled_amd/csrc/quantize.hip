@@ -527,7 +527,8 @@ quantize_t_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_
 // columns at once; the 64 lanes of a wave read one contiguous 256-byte row
 // (512 for fp32), so the reads are free of bank conflicts.  Each lane then
 // quantizes its four groups.  The results go back through the same LDS
-// (codes [128 columns][64 bytes], scales [128 columns][8 bytes]) so that the
+// (codes [128 columns][64 bytes], scales [128 columns][8 bytes], at padded
+// pitches) so that the
 // workgroup writes each column's 64 code bytes and 8 scale bytes with
 // neighbouring lanes on neighbouring bytes: written straight from the lanes,
 // every store instruction touched 64 cache lines, one per column.
@@ -626,17 +627,23 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
         group((cj == 0 ? ve : vo) + 16, lo[cj][1], hi[cj][1], by[cj][1]);
     }
 
-    // results into LDS (every lane has read its rows), then out column-wise
-    constexpr int kCodeRow = kTRG * 8;             // 64 code bytes per column
-    uint8_t* ocodes = tile;                        // [kTC][kCodeRow]
-    uint8_t* oscales = tile + kTC * kCodeRow;      // [kTC][kTRG]
+    // results into LDS (every lane has read its rows), then out column-wise:
+    // each column's 64 code bytes and 8 scale bytes, at pitches of 72 and 12
+    // bytes -- at 64 and 8, the lanes' writes (two columns apart) all fell on
+    // the same LDS banks
+    constexpr int kCodePitch = kTRG * 8 + 8;       // 64 code bytes per column
+    constexpr int kScalePitch = kTRG + 4;          // 8 scale bytes per column
+    uint8_t* ocodes = tile;                        // [kTC][kCodePitch]
+    uint8_t* oscales = tile + kTC * kCodePitch;    // [kTC][kScalePitch]
     __syncthreads();
 #pragma unroll
     for (int cj = 0; cj < 2; cj++) {
         const int lc = 2 * lane + cj;
-        *reinterpret_cast<uint4*>(ocodes + lc * kCodeRow + 2 * wave * 8) =
-            make_uint4(lo[cj][0], hi[cj][0], lo[cj][1], hi[cj][1]);
-        *reinterpret_cast<uint16_t*>(oscales + lc * kTRG + 2 * wave) =
+#pragma unroll
+        for (int ri = 0; ri < 2; ri++)
+            *reinterpret_cast<uint2*>(ocodes + lc * kCodePitch + (2 * wave + ri) * 8) =
+                make_uint2(lo[cj][ri], hi[cj][ri]);
+        *reinterpret_cast<uint16_t*>(oscales + lc * kScalePitch + 2 * wave) =
             (uint16_t)(by[cj][0] | (by[cj][1] << 8));
     }
     __syncthreads();
@@ -650,13 +657,17 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
             const int i = k * kThreads + tid;
             const int lc = i / 4, part = i % 4;
             const int64_t c = c0 + lc;
-            if (c < cols)
+            if (c < cols) {
+                const uint2 a = *reinterpret_cast<const uint2*>(ocodes + lc * kCodePitch + part * 16);
+                const uint2 b = *reinterpret_cast<const uint2*>(ocodes + lc * kCodePitch + part * 16 + 8);
                 *reinterpret_cast<uint4*>(codes + c * (rows / 2) + rgt * 8 + part * 16) =
-                    *reinterpret_cast<const uint4*>(ocodes + lc * kCodeRow + part * 16);
+                    make_uint4(a.x, a.y, b.x, b.y);
+            }
         }
-        if (tid < kTC && c0 + tid < cols)
-            *reinterpret_cast<uint2*>(scales + (c0 + tid) * rgs + rgt) =
-                *reinterpret_cast<const uint2*>(oscales + tid * kTRG);
+        if (tid < kTC && c0 + tid < cols) {
+            const uint32_t* sp = reinterpret_cast<const uint32_t*>(oscales + tid * kScalePitch);
+            *reinterpret_cast<uint2*>(scales + (c0 + tid) * rgs + rgt) = make_uint2(sp[0], sp[1]);
+        }
         return;
     }
     // codes: 8-byte pieces, 8 per column; scales: single bytes, 8 per column
@@ -667,8 +678,8 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
         const int64_t c = c0 + lc, rg = rgt + part;
         if (c < cols && rg < rgs) {
             *reinterpret_cast<uint2*>(codes + c * (rows / 2) + rg * 8) =
-                *reinterpret_cast<const uint2*>(ocodes + lc * kCodeRow + part * 8);
-            scales[c * rgs + rg] = oscales[lc * kTRG + part];
+                *reinterpret_cast<const uint2*>(ocodes + lc * kCodePitch + part * 8);
+            scales[c * rgs + rg] = oscales[lc * kScalePitch + part];
         }
     }
 }
