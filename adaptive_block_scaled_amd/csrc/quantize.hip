@@ -520,18 +520,18 @@ quantize_t_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_
 }
 
 // Tiled form of the x^T quantize, for 16-byte aligned rows: a workgroup
-// stages a tile of 128 rows x 128 columns of x in LDS with 16-byte loads (a
-// wave loads 4 rows, 256 contiguous bytes each for bf16), then each lane takes
-// a pair of adjacent columns and two consecutive row-groups (wave w: row-groups
-// 2w, 2w+1 of the tile) and reads its 32 rows as one word per row -- both
-// columns at once; the 64 lanes of a wave read one contiguous 256-byte row
-// (512 for fp32), so the reads are free of bank conflicts.  Each lane then
-// quantizes its four groups.  The results go back through the same LDS
-// (codes [128 columns][64 bytes], scales [128 columns][8 bytes], at padded
-// pitches) so that the
-// workgroup writes each column's 64 code bytes and 8 scale bytes with
-// neighbouring lanes on neighbouring bytes: written straight from the lanes,
-// every store instruction touched 64 cache lines, one per column.
+// takes a tile of 128 rows x 128 columns of x.  Each lane takes a pair of
+// adjacent columns and two consecutive row-groups (wave w: row-groups 2w,
+// 2w+1 of the tile) and loads its 32 rows straight from memory, one word per
+// row for both columns -- the 64 lanes of a wave read one contiguous 256-byte
+// row segment (512 for fp32) per load -- and quantizes its four groups.  The
+// results go through LDS (codes [128 columns][64 bytes], scales [128
+// columns][8 bytes], at padded pitches) so that the workgroup writes each
+// column's 64 code bytes and 8 scale bytes with neighbouring lanes on
+// neighbouring bytes: written straight from the lanes, every store instruction
+// touched 64 cache lines, one per column.  (Staging the input tile in LDS
+// first, with 16-byte loads, measured slower: it costs 32 KB of LDS per
+// workgroup and a full barrier before any group is quantized.)
 constexpr int kTR = 128, kTC = 128;  // tile rows (8 row-groups) and columns
 constexpr int kTRG = kTR / 16;       // row-groups per tile
 
@@ -541,76 +541,71 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                        float p_negexp, int64_t col_tiles, int wide_out) {
     constexpr int kElem = kBf16 ? 2 : 4;
-    constexpr int kRowBytes = kTC * kElem;        // 256 (bf16) or 512 (fp32)
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kRowBytes];
+    // results only: codes [kTC][kCodePitch], scales [kTC][kScalePitch]
+    constexpr int kCodePitch = kTRG * 8 + 8;       // 64 code bytes per column
+    constexpr int kScalePitch = kTRG + 4;          // 8 scale bytes per column
+    __shared__ __attribute__((aligned(16))) uint8_t obuf[kTC * (kCodePitch + kScalePitch)];
     __shared__ float2 recip[128];
-    if constexpr (kBf16) fill_recip(recip);
 
     const int64_t ct = blockIdx.x % col_tiles, rt = blockIdx.x / col_tiles;
     const int64_t c0 = ct * kTC, r0 = rt * kTR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
 
-    // stage: 16-byte chunks, row-major in LDS; out-of-range rows and columns
-    // read as zero (their groups are never stored).  Interior tiles skip the
-    // checks and address with 32-bit offsets from the tile's first element.
-    constexpr int kChunksPerRow = kRowBytes / 16, kElemsPerChunk = 16 / kElem;
-    constexpr int kLoads = kTR * kChunksPerRow / kThreads;
+    // this lane: tile columns 2*lane, 2*lane + 1 (one word per row for bf16,
+    // two for fp32); tile row-groups 2*wave, +1 (rows 32*wave .. +31).  The
+    // 64 lanes of a wave read one contiguous 256-byte (512 for fp32) row
+    // segment per load.  Out-of-range rows and columns read as zero (their
+    // groups are never stored); interior tiles skip the checks.
+    float ve[32], vo[32];
+    const int64_t gc = c0 + 2 * lane, gr = r0 + 32 * wave;
     if (r0 + kTR <= rows && c0 + kTC <= cols) {
-        const uint8_t* base = xb + (r0 * ld_x + c0) * kElem;
+        const uint8_t* p = xb + (gr * ld_x + gc) * kElem;
         const uint32_t ld_bytes = (uint32_t)(ld_x * kElem);
+        if constexpr (kBf16) {
+            uint32_t wd[32];
 #pragma unroll
-        for (int i = 0; i < kLoads; i++) {
-            const int chunk = i * kThreads + tid;
-            const int rr = chunk / kChunksPerRow, cc = chunk % kChunksPerRow;
-            *reinterpret_cast<uint4*>(tile + rr * kRowBytes + cc * 16) =
-                *reinterpret_cast<const uint4*>(base + rr * ld_bytes + cc * 16);
+            for (int rr = 0; rr < 32; rr++)
+                wd[rr] = *reinterpret_cast<const uint32_t*>(p + rr * ld_bytes);
+#pragma unroll
+            for (int rr = 0; rr < 32; rr++) {
+                ve[rr] = __uint_as_float(wd[rr] << 16);
+                vo[rr] = __uint_as_float(wd[rr] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 32; rr++) {
+                const uint2 wd = *reinterpret_cast<const uint2*>(p + rr * ld_bytes);
+                ve[rr] = __uint_as_float(wd.x);
+                vo[rr] = __uint_as_float(wd.y);
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < kLoads; i++) {
-            const int chunk = i * kThreads + tid;
-            const int rr = chunk / kChunksPerRow, cc = chunk % kChunksPerRow;
-            const int64_t r = r0 + rr, c = c0 + (int64_t)cc * kElemsPerChunk;
-            uint4 v = make_uint4(0, 0, 0, 0);
+        for (int rr = 0; rr < 32; rr++) {
+            const int64_t r = gr + rr;
+            float e = 0.0f, o = 0.0f;
             if (r < rows) {
-                const uint8_t* src = xb + (r * ld_x + c) * kElem;
-                if (c + kElemsPerChunk <= cols) {
-                    v = *reinterpret_cast<const uint4*>(src);
-                } else if (c < cols) {
-                    uint32_t w[4] = {0, 0, 0, 0};
-                    for (int e = 0; e < (int)(cols - c); e++) {
-                        const uint32_t val = kBf16
-                                                 ? (uint32_t)reinterpret_cast<const uint16_t*>(src)[e]
-                                                 : reinterpret_cast<const uint32_t*>(src)[e];
-                        if constexpr (kBf16)
-                            w[e >> 1] |= val << (16 * (e & 1));
-                        else
-                            w[e] = val;
-                    }
-                    v = make_uint4(w[0], w[1], w[2], w[3]);
+                const uint8_t* q = xb + (r * ld_x + gc) * kElem;
+                if constexpr (kBf16) {
+                    if (gc < cols) e = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(q) << 16);
+                    if (gc + 1 < cols)
+                        o = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(q + 2) << 16);
+                } else {
+                    if (gc < cols) e = *reinterpret_cast<const float*>(q);
+                    if (gc + 1 < cols) o = *reinterpret_cast<const float*>(q + 4);
                 }
             }
-            *reinterpret_cast<uint4*>(tile + rr * kRowBytes + cc * 16) = v;
+            ve[rr] = e;
+            vo[rr] = o;
         }
     }
-    __syncthreads();
-
-    // this lane: tile columns 2*lane, 2*lane + 1; tile row-groups 2*wave, +1
-    float ve[32], vo[32];  // the two columns, 32 rows
-#pragma unroll
-    for (int rr = 0; rr < 32; rr++) {
-        const uint8_t* p = tile + (32 * wave + rr) * kRowBytes + 2 * lane * kElem;
-        if constexpr (kBf16) {
-            const uint32_t wd = *reinterpret_cast<const uint32_t*>(p);
-            ve[rr] = __uint_as_float(wd << 16);
-            vo[rr] = __uint_as_float(wd & 0xFFFF0000u);
-        } else {
-            const uint2 wd = *reinterpret_cast<const uint2*>(p);
-            ve[rr] = __uint_as_float(wd.x);
-            vo[rr] = __uint_as_float(wd.y);
-        }
-    }
+    // the reciprocal table while the loads are in flight, behind an LDS-only
+    // barrier
+    if constexpr (kBf16) fill_recip(recip);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     auto group = [&](const float* src, uint32_t& lo, uint32_t& hi, uint32_t& byte) {
         float v[16];
 #pragma unroll
@@ -627,15 +622,11 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
         group((cj == 0 ? ve : vo) + 16, lo[cj][1], hi[cj][1], by[cj][1]);
     }
 
-    // results into LDS (every lane has read its rows), then out column-wise:
-    // each column's 64 code bytes and 8 scale bytes, at pitches of 72 and 12
-    // bytes -- at 64 and 8, the lanes' writes (two columns apart) all fell on
-    // the same LDS banks
-    constexpr int kCodePitch = kTRG * 8 + 8;       // 64 code bytes per column
-    constexpr int kScalePitch = kTRG + 4;          // 8 scale bytes per column
-    uint8_t* ocodes = tile;                        // [kTC][kCodePitch]
-    uint8_t* oscales = tile + kTC * kCodePitch;    // [kTC][kScalePitch]
-    __syncthreads();
+    // results into LDS, then out column-wise: each column's 64 code bytes and
+    // 8 scale bytes, at pitches of 72 and 12 bytes -- at 64 and 8, the lanes'
+    // writes (two columns apart) all fell on the same LDS banks
+    uint8_t* ocodes = obuf;
+    uint8_t* oscales = obuf + kTC * kCodePitch;
 #pragma unroll
     for (int cj = 0; cj < 2; cj++) {
         const int lc = 2 * lane + cj;
