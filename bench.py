@@ -16,7 +16,8 @@ again, back to back on its own, the
 dequantize of W's codes to bf16, the quantize of W^T (groups along dim 0),
 the quantize after a random-sign 16-point Hadamard rotation of each group,
 and the IF6 and IF3 quantizes and dequantizes.  `configs` times the smaller workloads at
-their own shapes (C2 and C3 quantizes, C4 GEMM), each cycling through
+their own shapes (C1 fp32 quantize and dequantize, C2 and C3 quantizes, C4
+GEMM), each cycling through
 enough buffer sets to stream from HBM.  `kernels` also holds two practical
 references timed the same way: a plain device-to-device copy of W's input
 for the memory-bound kernels (`frac_of_copy`), and the vendor library's
@@ -374,11 +375,26 @@ def time_other_configs(torch, if4, wl, dev, min_bytes=512 << 20):
         return {"shape": [R, C], "E": e, "buffer_sets": nset, "ms": round(ms, 5), "bytes": byts,
                 "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
+    # C1: fp32 256x256 through the exact kernel, and back to fp32 (tiny:
+    # the launch dominates; reported in microseconds)
+    t = wl.c1_mixed_fp32()
+    x1 = torch.from_numpy(t.values).to(dev)
+    c1, s1 = if4.quantize(x1, t.scale_exp)
+    y1 = torch.empty_like(x1)
+    ms_q = mean_launch_ms(torch, [lambda: if4.quantize(x1, t.scale_exp, out=(c1, s1))])
+    ms_d = mean_launch_ms(torch, [lambda: if4.dequantize(c1, s1, t.scale_exp, torch.float32, out=y1)])
+    out["C1_fp32_quantize_dequantize"] = {"shape": list(t.values.shape), "E": t.scale_exp,
+                                          "quantize_us": round(ms_q * 1e3, 2),
+                                          "dequantize_us": round(ms_d * 1e3, 2)}
+    del x1, c1, s1, y1
+
     t = wl.c2_activations()
     out["C2_quantize"] = quant_sets(t.values, t.scale_exp)
     t = wl.c3_rht_gradient()
     e3 = t.scale_exp
     out["C3_quantize"] = quant_sets(t.values, e3)
+    # at E = 0 every scale of this N(0, 1e-3) tensor underflows to zero
+    out["C3_quantize_E0"] = quant_sets(t.values, 0)
     # the same gradient before its rotation (same draws), rotated inside the
     # quantize, at the rotated tensor's exponent
     t, mask = wl.c3_raw_gradient()
