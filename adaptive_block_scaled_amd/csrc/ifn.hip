@@ -62,21 +62,24 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
 __device__ __forceinline__ int passes(float ax, float t, int k) {
     return (int)__float_as_uint(ax) + (k & 1) > (int)__float_as_uint(t) ? 1 : 0;
 }
-// the same for the INT boundary of |q| = k, given d = dd |x| - dn s (k + 1/2)
-// from one fma (its sign is exact and an exact zero is +0)
+// the same given the difference d = ax - t from one fma (its sign is exact and
+// an exact zero is +0): d > 0, or d == +0 for odd k -- the low bit or'ed into
+// d's bit pattern leaves a negative d negative
 __device__ __forceinline__ int passes_d(float d, int k) {
-    return (int)__float_as_uint(d) + (k & 1) > 0 ? 1 : 0;
+    return ((int)__float_as_uint(d) | (k & 1)) > 0 ? 1 : 0;
 }
 
-// E2M3 magnitude of index k and the midpoint between k and k + 1, exactly:
-// with e = max(k >> 3, 1), (k + 8 - 8e) 2^(e - 4) and (2k + 17 - 16e) 2^(e - 5)
+// E2M3 on fp32 bits: the index k = 8e + m (2 exponent bits with bias 1, 3
+// mantissa bits) placed at bit 20, k << 20, is the fp32 pattern with exponent
+// field e and mantissa m / 8 -- read as a float it equals the E2M3 magnitude
+// of k times 2^-126 for all 32 indices, E2M3's subnormals (e = 0) landing on
+// fp32's.  Setting bit 19 as well gives the midpoint between k and k + 1.
+// Multiplying by 2^126 makes either an exact normal float.
 __device__ __forceinline__ float e2m3_value(int k) {
-    const int e = k >> 3 > 1 ? k >> 3 : 1;
-    return __builtin_ldexpf((float)(k + 8 - 8 * e), e - 4);
+    return __uint_as_float((uint32_t)k << 20) * 0x1p126f;
 }
 __device__ __forceinline__ float e2m3_mid(int k) {
-    const int e = k >> 3 > 1 ? k >> 3 : 1;
-    return __builtin_ldexpf((float)(2 * k + 17 - 16 * e), e - 5);
+    return __uint_as_float(((uint32_t)k << 20) | (1u << 19)) * 0x1p126f;
 }
 
 // Every rounding below is "guess, then one exact comparison".  A guess
@@ -90,19 +93,17 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
                                                uint32_t (&out)[3], uint32_t& byte) {
     using F = Fmt<kBits>;
     constexpr float kInf = __builtin_inff();
-    float a = 0.0f;
-    bool finite = true;
+    // amax on the magnitudes' bit patterns, which order as the values do and
+    // put inf and NaN above every finite value
+    uint32_t abits = 0;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const float ax = __builtin_fabsf(v[i]);
-        finite &= ax <= 3.40282347e38f;
-        a = __builtin_fmaxf(a, ax);
-    }
+    for (int i = 0; i < 16; i++) abits = max(abits, __float_as_uint(v[i]) & 0x7FFFFFFFu);
     out[0] = out[1] = out[2] = 0;
-    if (!finite) {
+    if (abits >= 0x7F800000u) {
         byte = 0x7Fu;
         return;
     }
+    const float a = __uint_as_float(abits);
     // scale code RNE_E4M3(a 2^-E / top) over the 127 finite codes; the
     // boundary above code k is top (v_k + v_{k+1}) / 2 (4 + 5 bits, exact)
     const float ap = a * p_negexp;
@@ -144,21 +145,15 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
         int fi, q;
         float fvs;  // the float candidate's value times dd s, exact (at most 14 bits)
         if constexpr (kBits == 6) {
-            // guess: 8u below 1 (step 1/8), else 8 e + the top three
-            // mantissa bits (min/max instead of a select keep it
-            // branch-free), clamped to 30 so that the boundary above it
-            // exists; a guess is never above the correctly rounded index
+            // guess: the approximate quotient u = ax / s times 2^-126 (an
+            // fp32 subnormal below 1) truncated to the E2M3 bits above bit
+            // 20, clamped to 30 so that the boundary above it exists; a
+            // guess is never above the correctly rounded index.  The check
+            // takes the sign of ax - mid s from one fma.
             const float u = ax * r;
-            const int g = min((int)(__builtin_fminf(u, 1.0f) * 8.0f) +
-                                  (int)(__float_as_uint(__builtin_fmaxf(u, 1.0f)) >> 20) - 1016,
-                              kFMax - 1);
-            // with e = max(g >> 3, 1), the midpoint above g is nm 2^(e-5)
-            // and the magnitudes on either side are (nm -+ 1) 2^(e-5)
-            const int e = max(g >> 3, 1);
-            const int nm = 2 * g + 17 - 16 * e;
-            const int up = passes(ax, (float)nm * __builtin_ldexpf(s, e - 5), g);
-            fi = g + up;
-            fvs = (float)(nm - 1 + 2 * up) * __builtin_ldexpf(sdd, e - 5);
+            const int g = min((int)(__float_as_uint(__builtin_ldexpf(u, -126)) >> 20), kFMax - 1);
+            fi = g + passes_d(__builtin_fmaf(e2m3_mid(g), -s, ax), g);
+            fvs = e2m3_value(fi) * sdd;
             // INT: |q| > k  <=>  dd |x| > dn s (k + 1/2), the threshold
             // dn s k + dn s / 2 exact in one fma
             const int h = (int)__builtin_fminf(ax * rq, (float)(kQMax - 1));
