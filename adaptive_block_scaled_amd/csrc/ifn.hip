@@ -120,7 +120,12 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
     const float sdd = F::kDd * s, sdn = F::kDn * s;
     constexpr int kFMax = (1 << (kBits - 1)) - 1, kQMax = kFMax;
     // IF6: reciprocals for the guesses.  IF3: its three boundaries of each
-    // kind, counted directly.
+    // kind as fp32 values that ax is compared with directly.  The FP ones,
+    // s (fp(k) + fp(k + 1)) / 2, are exact; the INT ones, dn s (k + 1/2) / dd,
+    // are taken rounded down (exact when representable, as 2s is for k = 1):
+    // a float passes the rounded-down value exactly when it passes the true
+    // one, so "ax > t" decides an even k (ties stay down) and "ax >= t" the
+    // odd k = 1, whose boundaries are exact.
     const float r = __builtin_amdgcn_rcpf(s);
     const float rq = r * (F::kDd / F::kDn);
     const float sdn_half = 0.5f * sdn;
@@ -129,7 +134,10 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 #pragma unroll
         for (int k = 0; k < 3; k++) {
             tf[k] = s * (0.5f * (F::fp(k) + F::fp(k + 1)));
-            tq[k] = sdn * ((float)k + 0.5f);
+            // within an ulp of sdn (k + 1/2) / dd; one step down if above it
+            const float num = sdn * ((float)k + 0.5f);
+            const float w = num * (1.0f / F::kDd);
+            tq[k] = __builtin_fmaf(w, F::kDd, -num) > 0.0f ? __uint_as_float(__float_as_uint(w) - 1u) : w;
         }
     }
     float ef = 0.0f, ei = 0.0f;
@@ -143,7 +151,9 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
     for (int i = 0; i < 16; i++) {
         const float ax = __builtin_fabsf(v[i]);
         int fi, q;
-        float fvs;  // the float candidate's value times dd s, exact (at most 14 bits)
+        // the candidates' values times dd s and dd s dn / dd = dn s, exact
+        // (at most 14 significant bits)
+        float fvs, qsdn;
         if constexpr (kBits == 6) {
             // guess: the approximate quotient u = ax / s times 2^-126 (an
             // fp32 subnormal below 1) truncated to the E2M3 bits above bit
@@ -158,15 +168,19 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
             // dn s k + dn s / 2 exact in one fma
             const int h = (int)__builtin_fminf(ax * rq, (float)(kQMax - 1));
             q = h + passes_d(__builtin_fmaf(ax, F::kDd, -__builtin_fmaf((float)h, sdn, sdn_half)), h);
+            qsdn = (float)q * sdn;
         } else {
-            fi = passes(ax, tf[0], 0) + passes(ax, tf[1], 1) + passes(ax, tf[2], 2);
-            fvs = (float)((1 << fi) >> 1) * sdd;
-            q = 0;
-#pragma unroll
-            for (int k = 0; k < 3; k++) q += passes_d(__builtin_fmaf(ax, F::kDd, -tq[k]), k);
+            const bool f0 = ax > tf[0], f1 = ax >= tf[1], f2 = ax > tf[2];
+            const bool q0 = ax > tq[0], q1 = ax >= tq[1], q2 = ax > tq[2];
+            fi = (int)f0 + (int)f1 + (int)f2;
+            q = (int)q0 + (int)q1 + (int)q2;
+            // E2M0 on fp32 bits: index k << 23 read as a float is 0, 1, 2, 4
+            // times 2^-126 (exponent field k, k = 0 the zero)
+            fvs = (__uint_as_float((uint32_t)fi << 23) * 0x1p126f) * sdd;
+            qsdn = (float)q * sdn;
         }
         const float df = __builtin_fmaf(ax, F::kDd, -fvs);
-        const float di = __builtin_fmaf(ax, F::kDd, -((float)q * sdn));
+        const float di = __builtin_fmaf(ax, F::kDd, -qsdn);
         ef = __builtin_fmaf(df, df, ef);
         ei = __builtin_fmaf(di, di, ei);
         put(mf, (uint32_t)fi, kBits * i);
