@@ -17,9 +17,9 @@
 // little-endian 2*bits-byte code field.
 //
 // One group per thread, one workgroup per 256 groups, the thread's loads
-// issued first.  Every rounding is decided by exact comparisons against
-// thresholds that are exact in fp32 (the grids' midpoints times the scale),
-// ties to the even index -- valid for any fp32 input -- in branch-free code.
+// issued first.  Every rounding is decided exactly (exact comparisons, or the
+// exact sign of one fma), ties to the even index -- valid for any fp32 input
+// -- in branch-free code.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,12 +82,13 @@ __device__ __forceinline__ float e2m3_mid(int k) {
     return __uint_as_float(((uint32_t)k << 20) | (1u << 19)) * 0x1p126f;
 }
 
-// Every rounding below is "guess, then one exact comparison".  A guess
-// truncates an approximate quotient (at most a part in 2^21 off) to the grid
-// below it, which gives the correctly rounded index or the one below (the
-// grids are at least 2^-4 apart, relative); the comparison with the exact
-// fp32 threshold above the guess -- a product of at most 14 significant bits,
-// a normal number for the scales |E| <= 64 allows -- decides between them.
+// The scale code and IF6's indices are "guess, then one exact check".  A
+// guess truncates an approximate quotient (at most a part in 2^21 off) to the
+// grid below it, which gives the correctly rounded index or the one below
+// (the grids are at least 2^-4 apart, relative); comparing with the exact
+// boundary above the guess decides between them -- directly for the scale
+// (an fp32 product of at most 9 significant bits), by the sign of one fma
+// for the elements.  IF3 compares every element with its six boundaries.
 template <int kBits, int kMode>
 __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp, float p_negexp,
                                                uint32_t (&out)[3], uint32_t& byte) {
