@@ -194,7 +194,9 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
     byte = (uint32_t)sc | (use_int ? 0x80u : 0u);
 }
 
-template <int kBits, int kMode, bool kBf16>
+// kContig: rows back to back (ld = cols), so a group's offset is 16 g with
+// no division by the groups per row
+template <int kBits, int kMode, bool kBf16, bool kContig>
 __global__ void __launch_bounds__(kThreads)
 quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
@@ -202,8 +204,13 @@ quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64
     const int64_t ngroups = rows * gpr;
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t g = gid < ngroups - 1 ? gid : ngroups - 1;
-    const int64_t r = g / gpr;
-    const int64_t off = r * ld_x + (g - r * gpr) * 16;
+    int64_t off;
+    if constexpr (kContig) {
+        off = g * 16;
+    } else {
+        const int64_t r = g / gpr;
+        off = r * ld_x + (g - r * gpr) * 16;
+    }
     float v[16];
     if constexpr (kBf16) {
         const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
@@ -260,7 +267,7 @@ struct Fp {
     static constexpr float kDen = kBits == 6 ? 8.0f : 1.0f;  // fp(idx) * kDen is an integer
 };
 
-template <int kBits, bool kBf16>
+template <int kBits, bool kBf16, bool kContig>
 __global__ void __launch_bounds__(kThreads)
 dequantize_ifn_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       int64_t rows, int64_t gpr, void* __restrict__ y, int64_t ld_y, float p_exp) {
@@ -324,8 +331,13 @@ dequantize_ifn_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
         out[i] = __builtin_fmaf(a, e.x, a * e.y);
     }
     if (gid >= ngroups) return;
-    const int64_t r = gid / gpr;
-    const int64_t off = r * ld_y + (gid - r * gpr) * 16;
+    int64_t off;
+    if constexpr (kContig) {
+        off = gid * 16;
+    } else {
+        const int64_t r = gid / gpr;
+        off = r * ld_y + (gid - r * gpr) * 16;
+    }
     if constexpr (kBf16) {
         uint32_t o[8];
 #pragma unroll
@@ -353,9 +365,14 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uin
     const int64_t gpr = cols / 16;
     const int64_t blocks = (rows * gpr + kThreads - 1) / kThreads;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((quantize_ifn_kernel<kBits, kMode, kBf16>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales,
-                       pow2f(scale_exp), pow2f(-scale_exp));
+    if (ld_x == cols)
+        hipLaunchKernelGGL((quantize_ifn_kernel<kBits, kMode, kBf16, true>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales,
+                           pow2f(scale_exp), pow2f(-scale_exp));
+    else
+        hipLaunchKernelGGL((quantize_ifn_kernel<kBits, kMode, kBf16, false>),
+                           dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, rows, gpr, ld_x,
+                           codes, scales, pow2f(scale_exp), pow2f(-scale_exp));
     return hipGetLastError();
 }
 
@@ -381,14 +398,19 @@ hipError_t dispatch_dq(const uint8_t* codes, const uint8_t* scales, int64_t rows
     const int64_t gpr = cols / 16;
     const int64_t blocks = (rows * gpr + kThreads - 1) / kThreads;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (bf16)
-        hipLaunchKernelGGL((dequantize_ifn_kernel<kBits, true>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, codes, scales, rows, gpr, y, ld_y,
-                           pow2f(scale_exp));
-    else
-        hipLaunchKernelGGL((dequantize_ifn_kernel<kBits, false>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, codes, scales, rows, gpr, y, ld_y,
-                           pow2f(scale_exp));
+#define IF4_DQN(B, C)                                                                  \
+    hipLaunchKernelGGL((dequantize_ifn_kernel<kBits, B, C>), dim3((unsigned)blocks),            \
+                       dim3(kThreads), 0, stream, codes, scales, rows, gpr, y, ld_y,            \
+                       pow2f(scale_exp))
+    const bool contig = ld_y == cols;
+    if (bf16) {
+        if (contig) IF4_DQN(true, true);
+        else IF4_DQN(true, false);
+    } else {
+        if (contig) IF4_DQN(false, true);
+        else IF4_DQN(false, false);
+    }
+#undef IF4_DQN
     return hipGetLastError();
 }
 
