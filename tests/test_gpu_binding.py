@@ -79,6 +79,15 @@ def test_strided_outputs_accepted(if4, operands):
     want_c = if4.gemm(ac, as_, 0, wc, ws, 0)
     bigc = torch.full((64, 100), 7.0, device="cuda")
     c = if4.gemm(ac, as_, 0, wc, ws, 0, out=bigc[:, :96])
+    ifn = {}
+    for bits in (6, 3):
+        nc, ns = if4.quantize_ifn(a, bits)
+        bign = torch.full((64, 144), 7.0, dtype=torch.bfloat16, device="cuda")
+        ifn[bits] = (if4.dequantize_ifn(nc, ns, bits, 0, torch.bfloat16),
+                     if4.dequantize_ifn(nc, ns, bits, 0, out=bign[:, :128]), bign)
     torch.cuda.synchronize()
     assert torch.equal(y, want_y) and bool((big[:, 128:] == 7.0).all())
     assert torch.equal(c, want_c) and bool((bigc[:, 96:] == 7.0).all())
+    for bits, (want_n, got_n, bign) in ifn.items():
+        assert torch.equal(got_n, want_n), bits
+        assert bool((bign[:, 128:] == 7.0).all()), bits

@@ -183,3 +183,30 @@ def test_full_size_activation(oracle_mod):
         c, s = check_q(oracle_mod, x, bits, "bf16", e, label=t.name)
         gs = s.cpu().numpy()
         print(f"    IF{bits} int share {float((gs >= 0x80).mean()):.3f}", flush=True)
+
+
+def test_full_size_weight_sampled(oracle_mod):
+    """The FFN weight (28672 x 8192 bf16, Student-t) in IF6 and IF3 at the
+    exponent and in the launch configuration bench.py times: the whole tensor
+    goes through the kernels; 64 rows (the first two, the last, 61 seeded)
+    are checked against the oracle, codes, scale bytes and the bf16
+    dequantized values."""
+    _, t = wl.c5_ffn()
+    x = t.values
+    n = x.shape[0]
+    rows = np.unique(np.concatenate([[0, 1, n - 1],
+                                     np.random.default_rng(5).choice(n, 61, replace=False)]))
+    xd = to_dev(x, "bf16")
+    for bits in (6, 3):
+        print(f"[ifn] {t.name} IF{bits} E={t.scale_exp} sampled rows {len(rows)}", flush=True)
+        c, s = _if4().quantize_ifn(xd, bits, t.scale_exp)
+        y = _if4().dequantize_ifn(c, s, bits, t.scale_exp, torch.bfloat16)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(rows).cuda()
+        gc, gs = c[idx].cpu().numpy(), s[idx].cpu().numpy()
+        oc, os_ = oracle_mod.quantize_ifn(x[rows], bits, t.scale_exp, 0)
+        assert np.array_equal(gs, os_), bits
+        assert np.array_equal(gc, oc), bits
+        want = torch.from_numpy(oracle_mod.dequantize_ifn(oc, os_, bits, t.scale_exp))
+        assert torch.equal(y[idx].cpu(), want.to(torch.bfloat16)), bits
+        del c, s, y
