@@ -73,3 +73,25 @@ def test_full_size_c2(oracle_mod):
     t = wl.c2_activations()
     codes, scales = oracle_mod.quantize(t.values, t.scale_exp)
     compare(oracle_mod, codes, scales, t.scale_exp, t.name)
+
+
+def test_full_size_weight_sampled(oracle_mod):
+    """The FFN weight (28672 x 8192) dequantized to bf16 in the launch
+    configuration bench.py times: the whole tensor through the kernel, 64
+    rows (the first two, the last, 61 seeded) against the oracle's dequantize
+    of the same codes."""
+    from adaptive_block_scaled_amd import if4
+    _, t = wl.c5_ffn()
+    n = t.values.shape[0]
+    rows = np.unique(np.concatenate([[0, 1, n - 1],
+                                     np.random.default_rng(7).choice(n, 61, replace=False)]))
+    print(f"[dequantize] {t.name} E={t.scale_exp} sampled rows {len(rows)}", flush=True)
+    x = torch.from_numpy(t.values).to(torch.bfloat16).cuda()
+    codes, scales = if4.quantize(x, t.scale_exp)
+    y = if4.dequantize(codes, scales, t.scale_exp, torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).cuda()
+    c, s = codes[idx].cpu().numpy(), scales[idx].cpu().numpy()
+    want = oracle_mod.f32_to_bf16_bits(oracle_mod.dequantize(c, s, t.scale_exp))
+    got = y[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)

@@ -172,3 +172,24 @@ def test_rotated_operands_gemm(oracle_mod):
           flush=True)
     assert rel <= 1e-3
     assert rel_q < 0.2
+
+
+def test_weight_full_size_sampled(oracle_mod):
+    """Rotate + quantize of the FFN weight (28672 x 8192 bf16) with the sign
+    mask and exponent bench.py uses: the whole tensor through the kernel, 64
+    rows (the first two, the last, 61 seeded) against the oracle."""
+    _, t = wl.c5_ffn()
+    x = t.values
+    n = x.shape[0]
+    mask = wl.sign_mask(wl.random_signs(np.random.default_rng(0)))
+    e = t.scale_exp + 2
+    rows = np.unique(np.concatenate([[0, 1, n - 1],
+                                     np.random.default_rng(8).choice(n, 61, replace=False)]))
+    print(f"[quantize_rht] {t.name} mask={mask:#06x} E={e} sampled rows {len(rows)}", flush=True)
+    codes, scales = _if4().quantize_rht(to_dev(x, "bf16"), mask, e)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).cuda()
+    gc, gs = codes[idx].cpu().numpy(), scales[idx].cpu().numpy()
+    oc, os_ = oracle_mod.quantize_rht(x[rows], mask, e, 0, round_to_bf16=True)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, oc)
