@@ -91,3 +91,24 @@ def test_strided_outputs_accepted(if4, operands):
     for bits, (want_n, got_n, bign) in ifn.items():
         assert torch.equal(got_n, want_n), bits
         assert bool((bign[:, 128:] == 7.0).all()), bits
+
+
+def test_runs_on_the_callers_stream(if4, operands):
+    # every entry point enqueues on torch's current stream: the same path on
+    # a side stream (default priority) gives the default stream's results
+    a, ac, as_, wc, ws = operands
+    want = (if4.quantize(a), if4.dequantize(ac, as_, 0, torch.bfloat16),
+            if4.gemm(ac, as_, 0, wc, ws, 0), if4.quantize_ifn(a, 6), if4.quantize_t(a),
+            if4.quantize_rht(a, 0x1234))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = (if4.quantize(a), if4.dequantize(ac, as_, 0, torch.bfloat16),
+               if4.gemm(ac, as_, 0, wc, ws, 0), if4.quantize_ifn(a, 6), if4.quantize_t(a),
+               if4.quantize_rht(a, 0x1234))
+    side.synchronize()
+    torch.cuda.synchronize()
+    flat = lambda r: [t for x in r for t in (x if isinstance(x, tuple) else (x,))]
+    for g, w in zip(flat(got), flat(want)):
+        assert torch.equal(g, w)
