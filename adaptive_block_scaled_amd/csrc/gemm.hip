@@ -252,7 +252,7 @@ template <bool kWide>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
             const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
-            int64_t M, int64_t N, int64_t K, float* __restrict__ c, int64_t ldc, float out_scale,
+            int64_t M, int64_t N, int64_t K, float* __restrict__ c, int64_t ldc, int out_exp,
             int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -494,7 +494,10 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     }
 
     // epilogue: lane holds column lane%32 of each 32x32 block, rows
-    // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.  C is written
+    // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.  Each sum is
+    // scaled by 2^out_exp with one v_ldexp_f32 (a single rounding, and only
+    // where the result leaves the fp32 range: out_exp spans [-110, 146], more
+    // than one fp32 power of two can hold).  C is written
     // with non-temporal stores: nothing here reads it again, and dirty C
     // lines left in the caches slow whatever kernel runs next (a 470 MB
     // quantize launched after this GEMM took 125 us instead of 101 us)
@@ -507,7 +510,8 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
             for (int r = 0; r < 16; r++) {
                 const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < M && col < N)
-                    __builtin_nontemporal_store(acc[i][j][r] * out_scale, &c[row * ldc + col]);
+                    __builtin_nontemporal_store(__builtin_amdgcn_ldexpf(acc[i][j][r], out_exp),
+                                                &c[row * ldc + col]);
             }
         }
 }
@@ -522,7 +526,7 @@ __global__ void zero_kernel(float* __restrict__ c, int64_t M, int64_t N, int64_t
 template <bool kWide>
 hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                        const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, float* c,
-                       int64_t ldc, float out_scale, int64_t tiles_m, int64_t tiles_n,
+                       int64_t ldc, int out_exp, int64_t tiles_m, int64_t tiles_n,
                        hipStream_t stream) {
     // dynamic LDS above 64 KB must be allowed per kernel (idempotent, any device)
     hipError_t err = hipFuncSetAttribute((const void*)gemm_kernel<kWide>,
@@ -530,7 +534,7 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const ui
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(gemm_kernel<kWide>, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads),
                        SMEM_BYTES, stream, a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
-                       out_scale, (int)tiles_m, (int)tiles_n);
+                       out_exp, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
@@ -547,19 +551,19 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t 
     }
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
-    // 2^(a_exp + w_exp + 18) (each decoded operand carries 2^-9), exact; the
-    // exponent lies in [-110, 146] and is split into two factors
-    const int e = a_exp + w_exp + 18;
-    const float out_scale = pow2f(e / 2) * pow2f(e - e / 2);
+    // C = sum * 2^(a_exp + w_exp + 18): each decoded operand carries 2^-9.
+    // The exponent lies in [-110, 146], so it is applied per output in the
+    // kernel (ldexp), never as one fp32 factor, which would overflow.
+    const int out_exp = a_exp + w_exp + 18;
     // Wide fetches need 16-byte aligned code and scale rows and whole 4-slab
     // scale windows.
     const bool wide = K % (BK * kWin) == 0 && (uintptr_t)a_codes % 16 == 0 &&
                       (uintptr_t)w_codes % 16 == 0 && (uintptr_t)a_scales % 16 == 0 &&
                       (uintptr_t)w_scales % 16 == 0;
     return wide ? launch_tile<true>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
-                                    out_scale, tiles_m, tiles_n, stream)
+                                    out_exp, tiles_m, tiles_n, stream)
                 : launch_tile<false>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
-                                     out_scale, tiles_m, tiles_n, stream);
+                                     out_exp, tiles_m, tiles_n, stream);
 }
 
 }  // namespace if4

@@ -210,8 +210,10 @@ int if4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
  * c s' 2^-9 exactly, INT4 values fl16(|q| sigma 2^-9) with
  * sigma = fl16(fl32(s' * fl32(6/7))), the fp16 rounding of |q| sigma
  * (below 2^-5 to a multiple of 2^-15).  Products are accumulated in fp32 on
- * the matrix cores and C is scaled by 2^(a_exp + w_exp + 18) before the
- * fp32 store.
+ * the matrix cores, and each output sum is scaled by 2^(a_exp + w_exp + 18)
+ * with one ldexp before the fp32 store: exact while the result is a normal
+ * fp32 number, one rounding where it is subnormal, +-inf only where it
+ * overflows, and a zero sum stays +0 at every exponent pair.
  *   a_codes [M, K/2], w_codes [N, K/2]: device, 8-byte aligned
  *   a_scales [M, K/16], w_scales [N, K/16]: device
  *   c       device fp32 [M, N] with leading dimension ldc >= N, 4-byte aligned

@@ -58,27 +58,87 @@ def test_ragged_shapes(oracle_mod, mnk):
     assert err <= TOL
 
 
-def test_exact_when_products_exact(oracle_mod):
+# (a_exp, w_exp) pairs and the power of two the operands are scaled by so
+# that every exact result is a normal fp32 number: the sums of products lie in
+# [2^-18, 2^23] times the operand scale squared, and C = sum * 2^(a_exp + w_exp)
+EXP_CASES = [((0, 0), 0), ((-3, 5), 0), ((64, 64), -8), ((55, 55), -4), ((64, -64), 0),
+             ((-64, 64), 0), ((-64, -64), 4)]
+
+
+def _fp4_grid_operands(rng, M, N, K, scale_pow):
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    a = grid[rng.integers(0, 8, (M, K))] * np.where(rng.random((M, K)) < .5, -1, 1)
+    w = grid[rng.integers(0, 8, (N, K))] * np.where(rng.random((N, K)) < .5, -1, 1)
+    a[:, ::16] = 6
+    w[:, ::16] = -6
+    a = (a * 0.5 * 2.0 ** scale_pow).astype(np.float32)
+    w = (w * 2.0 * 2.0 ** scale_pow).astype(np.float32)
+    a[3] = 0.0  # an all-zero row of A: its row of C must be +0
+    return a, w
+
+
+@pytest.mark.parametrize("K", [16, 32, 48, 160, 256, 512, 1024])
+def test_exact_when_products_exact(oracle_mod, K):
     """FP4-only operands with power-of-two scales: products are small dyadic
     numbers and partial sums stay exact in fp32, so C must equal the exact
-    result bit for bit."""
-    rng = np.random.default_rng(12)
-    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
-    for K in (16, 32, 48, 160):
-        M, N = 70, 90
-        a = grid[rng.integers(0, 8, (M, K))] * np.where(rng.random((M, K)) < .5, -1, 1)
-        w = grid[rng.integers(0, 8, (N, K))] * np.where(rng.random((N, K)) < .5, -1, 1)
-        a[:, ::16] = 6
-        w[:, ::16] = -6
-        a = (a * 0.5).astype(np.float32)
-        w = (w * 2.0).astype(np.float32)
+    result bit for bit, at every exponent pair the C ABI accepts the extremes
+    of.  K = 256, 512 and 1024 (multiples of 256, rows 16-byte aligned in
+    fresh allocations) take the wide-fetch path the benchmark runs; the others
+    the per-word path.  Row 3 of A is zero and must give +0 (not -0 or NaN)."""
+    rng = np.random.default_rng(12 + K)
+    M, N = 70, 90
+    for (ea, ew), pw in EXP_CASES:
+        a, w = _fp4_grid_operands(rng, M, N, K, pw)
         ac, as_ = oracle_mod.quantize(a, 0)
         wc, ws = oracle_mod.quantize(w, 0)
         assert not (as_ & 0x80).any() and not (ws & 0x80).any()
-        for ea, ew in ((0, 0), (-3, 5)):
-            got = gpu_gemm(ac, as_, ea, wc, ws, ew)
-            ref = (a.astype(np.float64) @ w.T.astype(np.float64)) * 2.0 ** (ea + ew)
-            assert np.array_equal(got.astype(np.float64), ref), (K, ea, ew)
+        got = gpu_gemm(ac, as_, ea, wc, ws, ew)
+        exact = a.astype(np.float64) @ w.T.astype(np.float64)
+        ref = exact * 2.0 ** (ea + ew)
+        nz = ref != 0
+        assert np.all(np.abs(ref[nz]) >= 2.0 ** -126) and np.all(np.abs(ref) < 2.0 ** 128)
+        assert np.array_equal(got.astype(np.float64), ref), (K, ea, ew)
+        # the oracle's fp64 GEMM of the same codes agrees with the exact product
+        assert np.array_equal(oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew), ref)
+        assert (got[3] == 0).all() and not np.signbit(got[3]).any(), (K, ea, ew)
+
+
+@pytest.mark.parametrize("exps", [(64, 64), (55, 55), (64, -64), (-64, -64)])
+@pytest.mark.parametrize("K", [512, 528])
+def test_extreme_exponents_against_oracle(oracle_mod, exps, K):
+    """Adaptive (FP4 and INT4) operands at the largest and smallest exponent
+    pairs the C ABI accepts, drawn so that C is representable: scale bytes
+    small for (64, 64) and (55, 55), large for (-64, -64).  The output is
+    2^(a_exp + w_exp + 18) times the fp32 sums, applied per output, so it
+    must meet the same tolerance as at E = 0, with no inf and no NaN; an
+    all-zero row of A comes back +0.  K = 512 runs the wide path, 528 the
+    per-word path."""
+    ea, ew = exps
+    rng = np.random.default_rng(ea * 3 + ew + K)
+    M, N = 96, 320
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    # E4M3 codes 0x01-0x08 (2^-9 .. 2^-6) at (64, 64), 0x01-0x30 (up to 0.5)
+    # at (55, 55), 0x60-0x7E (32 .. 448) at (-64, -64), any finite code at
+    # (64, -64); bit 7 (INT4) random
+    lo, hi = {(64, 64): (1, 0x08), (55, 55): (1, 0x30), (64, -64): (1, 0x7E),
+              (-64, -64): (0x60, 0x7E)}[exps]
+    as_ = (rng.integers(lo, hi + 1, (M, K // 16)) | (rng.integers(0, 2, (M, K // 16)) << 7)
+           ).astype(np.uint8)
+    ws = (rng.integers(lo, hi + 1, (N, K // 16)) | (rng.integers(0, 2, (N, K // 16)) << 7)
+          ).astype(np.uint8)
+    ac[5] = 0
+    as_[5] = 0
+    print(f"[gemm] exponents {exps} K={K} INT4 share {((as_ & 0x80) != 0).mean():.2f}",
+          flush=True)
+    got = gpu_gemm(ac, as_, ea, wc, ws, ew)
+    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew)
+    assert np.isfinite(ref).all() and np.abs(ref).max() < 2.0 ** 127
+    assert np.isfinite(got).all(), exps
+    assert (got[5] == 0).all() and not np.signbit(got[5]).any()
+    err = rel_fro(got, ref)
+    print(f"    rel fro {err:.3e}", flush=True)
+    assert err <= TOL
 
 
 def test_k_zero_writes_zeros():
@@ -124,20 +184,31 @@ def test_more_tiles_than_compute_units(oracle_mod, mnk):
 
 
 def test_c4_full_size(oracle_mod):
+    """The 4096^3 workload, every one of the 16.8 M outputs against the fp64
+    oracle: the relative Frobenius error over all of C, and over each
+    256 x 256 output tile (the unit one workgroup computes)."""
     a, w = wl.c4_gemm()
     ea, ew = a.scale_exp, w.scale_exp
     print(f"[gemm] c4 4096^3 E_A={ea} E_W={ew}", flush=True)
     ac, as_ = oracle_mod.quantize(a.values, ea)
     wc, ws = oracle_mod.quantize(w.values, ew)
-    got = gpu_gemm(ac, as_, ea, wc, ws, ew)
-    rows = np.sort(np.random.default_rng(7).choice(4096, 256, replace=False))
-    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew, rows=rows)
-    err = rel_fro(got[rows], ref)
-    print(f"    rel fro on 256 sampled rows x 4096 cols: {err:.3e}", flush=True)
+    got = gpu_gemm(ac, as_, ea, wc, ws, ew).astype(np.float64)
+    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew)
+    err = rel_fro(got, ref)
+    print(f"    rel fro on all 4096 x 4096 outputs: {err:.3e}", flush=True)
     assert err <= TOL
+    d = (got - ref).reshape(16, 256, 16, 256)
+    r = ref.reshape(16, 256, 16, 256)
+    tile_err = np.sqrt((d ** 2).sum(axis=(1, 3)) / (r ** 2).sum(axis=(1, 3)))
+    print(f"    worst 256x256 tile {tile_err.max():.3e}", flush=True)
+    assert tile_err.max() <= TOL
 
 
 def test_c5_full_size(oracle_mod):
+    """The FFN workload (M=8192, N=28672, K=8192): one seeded row in every
+    256-row M-tile plus the first and last rows, each against all 28672
+    columns; the error is checked over the sample and over every 256-column
+    block of it, so each of the 3584 output tiles is compared on its own."""
     a, w = wl.c5_ffn()
     ea, ew = a.scale_exp, w.scale_exp
     print(f"[gemm] c5 M=8192 N=28672 K=8192 E_A={ea} E_W={ew}", flush=True)
@@ -146,8 +217,19 @@ def test_c5_full_size(oracle_mod):
     del a, w
     got = gpu_gemm(ac, as_, ea, wc, ws, ew)
     rng = np.random.default_rng(8)
-    rows = np.sort(rng.choice(8192, 48, replace=False))
-    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew, rows=rows)
-    err = rel_fro(got[rows], ref)
-    print(f"    rel fro on 48 sampled rows x 28672 cols: {err:.3e}", flush=True)
+    rows = sorted({t * 256 + int(rng.integers(0, 256)) for t in range(32)} | {0, 8191})
+    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew, rows=np.array(rows))
+    g = got[rows].astype(np.float64)
+    err = rel_fro(g, ref)
+    print(f"    rel fro on {len(rows)} rows (every M-tile) x 28672 cols: {err:.3e}", flush=True)
     assert err <= TOL
+    worst = 0.0
+    for t in range(32):  # the sampled rows of M-tile t, each 256-column block
+        sel = [i for i, r in enumerate(rows) if r // 256 == t]
+        assert sel, t
+        for j in range(0, 28672, 256):
+            blk = np.linalg.norm(g[sel, j:j + 256] - ref[sel, j:j + 256]) / np.linalg.norm(
+                ref[sel, j:j + 256])
+            worst = max(worst, blk)
+            assert blk <= 4 * TOL, (t, j, blk)
+    print(f"    worst tile block {worst:.3e}", flush=True)
