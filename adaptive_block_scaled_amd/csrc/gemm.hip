@@ -93,53 +93,107 @@ __device__ __forceinline__ GroupScale lookup_scale(const uint8_t* smem, uint32_t
     return s;
 }
 
-// Decode one code word (8 nibbles = half a group, element 2j in the low
-// nibble of byte j) into 8 fp16 operands in K order.
-__device__ __forceinline__ half8 decode_half(uint32_t w, GroupScale s) {
-    const uint32_t he = ((w & 0x07070707u) << s.sh) | ((w << 4) & 0x80808080u);
-    const uint32_t ho = (((w >> 4) & 0x07070707u) << s.sh) | (w & 0x80808080u);
-    // v_perm: byte j of `he` -> bits 15:8, byte j of `ho` -> bits 31:24, zeros below
-    uint4 o;
-    o.x = pk_mul(__builtin_amdgcn_perm(ho, he, 0x040C000Cu), s.sig2);
-    o.y = pk_mul(__builtin_amdgcn_perm(ho, he, 0x050C010Cu), s.sig2);
-    o.z = pk_mul(__builtin_amdgcn_perm(ho, he, 0x060C020Cu), s.sig2);
-    o.w = pk_mul(__builtin_amdgcn_perm(ho, he, 0x070C030Cu), s.sig2);
-    return __builtin_bit_cast(half8, o);
+// Decode the two code words of one group (w0: elements 0-7, w1: elements
+// 8-15; element 2j in the low nibble of byte j) into 16 fp16 operands in K
+// order.  Per word, two bytes hold the fp16 high bytes of its even and odd
+// elements: he = [sign | magnitude << sh] of the low nibbles, ho the same
+// for the high nibbles.  The magnitudes are shifted as one 64-bit word per
+// group (the shift moves no bit across a nibble: bit 3 of every nibble is
+// cleared first), and each byte is assembled by one bit-field insert under
+// the mask 0x0F0F0F0F: the low half from the shifted magnitudes, the high
+// half from the sign bits (moved up by 4 for the even elements; the bits a
+// 64-bit shift carries across the word boundary land in masked-off
+// positions).  27 VALU instructions per group.
+// m ? a : b, bit by bit: one v_bitop3_b32 (truth table over (a, b, m)).
+__device__ __forceinline__ uint32_t bit_select(uint32_t a, uint32_t b, uint32_t m) {
+    return __builtin_amdgcn_bitop3_b32(a, b, m, 0xE4);
+}
+// 64-bit shifts by 4 as single instructions (full rate on gfx950; the
+// compiler otherwise splits them into two 32-bit operations).
+__device__ __forceinline__ uint64_t shr64_by4(uint64_t x) {
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, 4, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+__device__ __forceinline__ uint64_t shl64_by4(uint64_t x) {
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, 4, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+__device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, GroupScale s, half8& o0,
+                                             half8& o1) {
+    constexpr uint32_t kLo = 0x0F0F0F0Fu;  // low nibble of every byte
+    const uint32_t m0 = w0 & 0x77777777u, m1 = w1 & 0x77777777u;
+    const uint64_t ms = ((uint64_t)m1 << 32 | m0) << s.sh;
+    const uint64_t mr = shr64_by4(ms);
+    const uint32_t g0 = w0 ^ m0, g1 = w1 ^ m1;  // sign bits (bits 3 and 7 of each byte)
+    const uint64_t g4 = shl64_by4((uint64_t)g1 << 32 | g0);
+    const uint32_t he0 = bit_select((uint32_t)ms, (uint32_t)g4, kLo);
+    const uint32_t he1 = bit_select((uint32_t)(ms >> 32), (uint32_t)(g4 >> 32), kLo);
+    const uint32_t ho0 = bit_select((uint32_t)mr, g0, kLo);
+    const uint32_t ho1 = bit_select((uint32_t)(mr >> 32), g1, kLo);
+    // v_perm: byte j of he -> bits 15:8, byte j of ho -> bits 31:24, zeros below
+    uint4 r0, r1;
+    r0.x = pk_mul(__builtin_amdgcn_perm(ho0, he0, 0x040C000Cu), s.sig2);
+    r0.y = pk_mul(__builtin_amdgcn_perm(ho0, he0, 0x050C010Cu), s.sig2);
+    r0.z = pk_mul(__builtin_amdgcn_perm(ho0, he0, 0x060C020Cu), s.sig2);
+    r0.w = pk_mul(__builtin_amdgcn_perm(ho0, he0, 0x070C030Cu), s.sig2);
+    r1.x = pk_mul(__builtin_amdgcn_perm(ho1, he1, 0x040C000Cu), s.sig2);
+    r1.y = pk_mul(__builtin_amdgcn_perm(ho1, he1, 0x050C010Cu), s.sig2);
+    r1.z = pk_mul(__builtin_amdgcn_perm(ho1, he1, 0x060C020Cu), s.sig2);
+    r1.w = pk_mul(__builtin_amdgcn_perm(ho1, he1, 0x070C030Cu), s.sig2);
+    o0 = __builtin_bit_cast(half8, r0);
+    o1 = __builtin_bit_cast(half8, r1);
 }
 
 // ---------------------------------------------------------------------------
 // Operand fetch.  The vector memory path costs about one cycle per distinct
 // cache line an instruction touches, so loads are shaped to touch few lines:
-// an A lane's 16 code bytes share their 32-byte row segment with its partner
-// lane (32 lines per instruction), two W lanes load the two halves of one
-// row's 32-byte slab (32 lines), and scale bytes are fetched 16 at a time,
-// four slabs' worth per row.
+// the two lanes l and l+32 load the two 16-byte halves of one row's 32-byte
+// slab (A and W alike, 32 lines per instruction), and scale bytes are
+// fetched 16 at a time, four slabs' worth per row.
 //
 // kWide: 16-byte aligned code and scale rows, K a multiple of 256 (whole
-// scale windows).  Otherwise every word and byte is fetched on its own,
+// scale windows).  The wide path reads through buffer resources based at
+// the tile's first row: each lane's row offset is fixed (rows past M or N
+// take the last row's; those outputs are never stored) and the slab's
+// offset is one scalar register, clamped to the last slab on the scalar
+// unit, so a fetch costs no vector address arithmetic and every access stays
+// inside its operand.  Otherwise every word and byte is fetched on its own,
 // clamped into the row, and groups past K decode with a zero multiplier.
+
+// Word 3 of a buffer resource for plain byte-addressed dword loads on gfx9
+// class chips (no format conversion, no swizzle).
+constexpr int kRawBufferFlags = 0x00020000;
+
+struct Operand {
+    __amdgpu_buffer_rsrc_t codes, scales;
+    uint32_t code_off[2], scale_off[2];  // this lane's two rows
+};
 
 // Codes of one slab for one lane: A blocks i = 0, 1 (row lane%32 of each,
 // groups 2h, 2h+1 with h = lane/32) and W rows k = 0, 1 (groups 2q, 2q+1
-// with q = lane%2).
+// with q = lane/32).
 template <bool kWide>
 struct SlabCodes;
 
 template <>
 struct SlabCodes<true> {
     uint4 a[2], w[2];
-    __device__ __forceinline__ void load(const uint8_t* const* acp, const uint8_t* const* asp,
-                                         const uint8_t* const* wcp, const uint8_t* const* wsp,
-                                         int64_t slab, int h, int q, int64_t gpr) {
-        (void)asp, (void)wsp, (void)h, (void)q, (void)gpr;
+    __device__ __forceinline__ void load(const Operand& A, const Operand& W, int64_t slab) {
+        const int so = (int)slab * 32;
 #pragma unroll
-        for (int i = 0; i < 2; i++) a[i] = *reinterpret_cast<const uint4*>(acp[i] + slab * 32);
+        for (int i = 0; i < 2; i++)
+            a[i] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(A.codes, A.code_off[i], so, 0));
 #pragma unroll
-        for (int k = 0; k < 2; k++) w[k] = *reinterpret_cast<const uint4*>(wcp[k] + slab * 32);
+        for (int k = 0; k < 2; k++)
+            w[k] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(W.codes, W.code_off[k], so, 0));
     }
-    // A block i, MFMA step t: word (group 2h + t/2, half t%2)
-    __device__ __forceinline__ uint32_t aword(int i, int t) const {
-        return t == 0 ? a[i].x : t == 1 ? a[i].y : t == 2 ? a[i].z : a[i].w;
+    // A block i, word u = 2 * (group - 2h) + half
+    __device__ __forceinline__ uint32_t aword(int i, int u) const {
+        return u == 0 ? a[i].x : u == 1 ? a[i].y : u == 2 ? a[i].z : a[i].w;
     }
     // W row k, word u = 2 * (group - 2q) + half
     __device__ __forceinline__ uint32_t wword(int k, int u) const {
@@ -150,32 +204,29 @@ struct SlabCodes<true> {
 template <>
 struct SlabCodes<false> {
     uint32_t a[2][4], w[2][4];
-    uint32_t ab[2][4], wb[2][2];  // scale bytes
+    uint32_t ab[2][2], wb[2][2];  // scale bytes per row and group
+    // acp/asp, wcp/wsp: code and scale rows of this lane (clamped into the
+    // operand); gpr: groups per row
     __device__ __forceinline__ void load(const uint8_t* const* acp, const uint8_t* const* asp,
                                          const uint8_t* const* wcp, const uint8_t* const* wsp,
-                                         int64_t slab, int h, int q, int64_t gpr) {
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const int64_t g = slab * kGroups + 2 * h + (t >> 1);
-                const int64_t gc = g < gpr ? g : gpr - 1;
-                a[i][t] = *reinterpret_cast<const uint32_t*>(acp[i] + gc * 8 + 4 * (t & 1));
-                ab[i][t] = asp[i][gc];
-            }
+                                         int64_t slab, int h, int64_t gpr) {
 #pragma unroll
         for (int k = 0; k < 2; k++)
 #pragma unroll
             for (int gg = 0; gg < 2; gg++) {
-                const int64_t g = slab * kGroups + 2 * q + gg;
+                const int64_t g = slab * kGroups + 2 * h + gg;
                 const int64_t gc = g < gpr ? g : gpr - 1;
-                const uint2 v = *reinterpret_cast<const uint2*>(wcp[k] + gc * 8);
-                w[k][2 * gg] = v.x;
-                w[k][2 * gg + 1] = v.y;
+                const uint2 va = *reinterpret_cast<const uint2*>(acp[k] + gc * 8);
+                a[k][2 * gg] = va.x;
+                a[k][2 * gg + 1] = va.y;
+                ab[k][gg] = asp[k][gc];
+                const uint2 vw = *reinterpret_cast<const uint2*>(wcp[k] + gc * 8);
+                w[k][2 * gg] = vw.x;
+                w[k][2 * gg + 1] = vw.y;
                 wb[k][gg] = wsp[k][gc];
             }
     }
-    __device__ __forceinline__ uint32_t aword(int i, int t) const { return a[i][t]; }
+    __device__ __forceinline__ uint32_t aword(int i, int u) const { return a[i][u]; }
     __device__ __forceinline__ uint32_t wword(int k, int u) const { return w[k][u]; }
 };
 
@@ -183,12 +234,16 @@ struct SlabCodes<false> {
 // per W row; word u holds slab u's four groups.
 struct WinScales {
     uint4 a[2], w[2];
-    __device__ __forceinline__ void load(const uint8_t* const* asp, const uint8_t* const* wsp,
-                                         int64_t win) {
+    __device__ __forceinline__ void load(const Operand& A, const Operand& W, int64_t win) {
+        const int so = (int)win * 16;
 #pragma unroll
-        for (int i = 0; i < 2; i++) a[i] = *reinterpret_cast<const uint4*>(asp[i] + win * 16);
+        for (int i = 0; i < 2; i++)
+            a[i] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(A.scales, A.scale_off[i], so, 0));
 #pragma unroll
-        for (int k = 0; k < 2; k++) w[k] = *reinterpret_cast<const uint4*>(wsp[k] + win * 16);
+        for (int k = 0; k < 2; k++)
+            w[k] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(W.scales, W.scale_off[k], so, 0));
     }
 };
 
@@ -198,7 +253,7 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
 
 // IF4 x IF4 GEMM kernel.
 //
-// Decode (decode_half): a code nibble becomes the high byte of an fp16
+// Decode (decode_group): a code nibble becomes the high byte of an fp16
 // number by shifts and masks alone -- FP4 s.e1e0.m -> s.000e1e0.m (the fp16
 // value c * 2^-14; e = 0 lands on the fp16 subnormals, which keeps it
 // exact), INT4 s.mmm -> s.0000.mmm (|q| * 2^-16).  v_perm_b32 spreads four
@@ -227,7 +282,8 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
 // tile is shared by the four waves and goes through LDS: each thread decodes
 // two groups of two W rows per slab into a double-buffered 2 x 32 KB tile
 // in MFMA fragment order (frag_off), which a wave reads as contiguous 1 KB
-// ds_read_b128s.
+// ds_read_b128s (its stores: 64 lanes on 1 KB of consecutive 16-byte
+// pieces, no bank conflicts).
 //
 // Pipeline: while the MFMAs of K slab s run, each wave decodes slab s+1
 // (its A registers, its W share into the other LDS buffer) and fetches the
@@ -239,15 +295,16 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
 // Within a slab, each MFMA step runs four sub-blocks of four MFMAs: (A block
 // 0, W blocks 0..3), (1, 0..3), (0, 4..7), (1, 4..7); the eight W fragments
 // of the next step are read into a second register set at the start of the
-// step, a whole step before their use.
-// Each sub-block carries one code-word decode (about 16 VALU instructions):
-// A block 1's operand of step t-1 in sub-block 0 (for step 0, from a word
-// kept across the barrier), W words in sub-blocks 1 and 2, A block 0's
-// operand of step t in sub-block 3.  The scale-table lookups of a step's
-// decodes are issued at the start of the step before (LDS operations
-// complete in order, so a lookup issued after the fragment reads would make
-// its consumer wait for them too).  Rows past M or N load their nearest
-// in-range row (those outputs are never stored).
+// step, a whole step before their use.  Every step decodes two groups: one
+// of W (row t/2, group 2q + t%2 of the next slab, stored in sub-blocks 1
+// and 2), and one of A, as soon as both of its operand registers are free --
+// A block 1's words 2-3 of the running slab in step 0 (kept across the
+// barrier) and words 0-1 of the next slab in step 2 (sub-block 0, after
+// their last use in steps 0 and 1), A block 0's words 0-1 and 2-3 of the
+// next slab in steps 1 and 3 (sub-block 3, after their last use).  The
+// scale-table lookups of a step's decodes are issued at the start of the step
+// before (LDS operations complete in order, so a lookup issued after the
+// fragment reads would make its consumer wait for them too).
 template <bool kWide>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -277,29 +334,55 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t kb = K / 2, gpr = K / 16;
 
-    // A rows of this lane: row lane%32 of the wave's two 32-row blocks
+    // rows of this lane: A rows 64w + 32i + lane%32 of the tile (i = 0, 1),
+    // W rows 64w + 32k + lane%32 (k = 0, 1); K-half h = q = lane/32
     const int h = lane >> 5, hs = 16 * h;
+    const int q = h, qs = hs;
+    const int rl = lane & 31;
+    int wr_row[2];
+#pragma unroll
+    for (int k = 0; k < 2; k++) wr_row[k] = 64 * wave + 32 * k + rl;
+
+    Operand opA, opW;
     const uint8_t* acp[2];
     const uint8_t* asp[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int64_t r = m0 + 64 * wave + 32 * i + (lane & 31);
-        const int64_t rc = r < M ? r : M - 1;
-        acp[i] = a_codes + rc * kb + (kWide ? 16 * h : 0);
-        asp[i] = a_scales + rc * gpr;
-    }
-    // W rows of this thread: tile rows 64w + 32k + lane/2, groups 2q, 2q+1
-    const int q = lane & 1, qs = 16 * q;
-    int wr_row[2];
     const uint8_t* wcp[2];
     const uint8_t* wsp[2];
+    if constexpr (kWide) {
+        // resources based at the tile's first row, sized to the tile's rows
+        // that exist (offsets fit 31 bits: 256 rows of K/2 bytes, checked on
+        // launch)
+        const int64_t arows = M - m0 < BM ? M - m0 : BM, wrows = N - n0 < BN ? N - n0 : BN;
+        opA.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(a_codes + m0 * kb), 0,
+                                                       (int)(arows * kb), kRawBufferFlags);
+        opA.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(a_scales + m0 * gpr), 0,
+                                                        (int)(arows * gpr), kRawBufferFlags);
+        opW.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(w_codes + n0 * kb), 0,
+                                                       (int)(wrows * kb), kRawBufferFlags);
+        opW.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(w_scales + n0 * gpr), 0,
+                                                        (int)(wrows * gpr), kRawBufferFlags);
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-        wr_row[k] = 64 * wave + 32 * k + (lane >> 1);
-        const int64_t r = n0 + wr_row[k];
-        const int64_t rc = r < N ? r : N - 1;
-        wcp[k] = w_codes + rc * kb + (kWide ? 16 * q : 0);
-        wsp[k] = w_scales + rc * gpr;
+        for (int i = 0; i < 2; i++) {
+            const int ra = 64 * wave + 32 * i + rl, rw = wr_row[i];
+            const uint32_t rac = (uint32_t)(ra < arows ? ra : arows - 1);
+            const uint32_t rwc = (uint32_t)(rw < wrows ? rw : wrows - 1);
+            opA.code_off[i] = rac * (uint32_t)kb + 16 * h;
+            opA.scale_off[i] = rac * (uint32_t)gpr;
+            opW.code_off[i] = rwc * (uint32_t)kb + 16 * q;
+            opW.scale_off[i] = rwc * (uint32_t)gpr;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int64_t r = m0 + 64 * wave + 32 * i + rl;
+            const int64_t rc = r < M ? r : M - 1;
+            acp[i] = a_codes + rc * kb;
+            asp[i] = a_scales + rc * gpr;
+            const int64_t rw = n0 + wr_row[i];
+            const int64_t rwc = rw < N ? rw : N - 1;
+            wcp[i] = w_codes + rwc * kb;
+            wsp[i] = w_scales + rwc * gpr;
+        }
     }
 
     float16v acc[2][8];
@@ -317,73 +400,94 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     fill_scale_table(smem, tid);
     lds_barrier();
 
-    // Scale of A block i / W row k, group selected by t / gg, in slab
-    // `slab` = window slot u of a window's scales (wide) or from the slab's
-    // own bytes; groups past K exist only without whole slabs.
+    // Scale of A block i / W row k, group 2h + g / 2q + g, in slab `slab` =
+    // window slot u of a window's scales (wide) or from the slab's own bytes;
+    // groups past K exist only without whole slabs.
     auto a_scale = [&](const SlabCodes<kWide>& x, const WinScales& win, int u, int64_t slab,
-                       int i, int t) {
+                       int i, int g) {
         uint32_t b;
         if constexpr (kWide) {
-            b = (word_of(win.a[i], u) >> (hs + 8 * (t >> 1))) & 0xFFu;
+            b = (word_of(win.a[i], u) >> (hs + 8 * g)) & 0xFFu;
         } else {
-            const bool past = slab * kGroups + 2 * h + (t >> 1) >= gpr;
-            b = past ? kZeroScale : x.ab[i][t];
+            const bool past = slab * kGroups + 2 * h + g >= gpr;
+            b = past ? kZeroScale : x.ab[i][g];
         }
         return lookup_scale(smem, b);
     };
     auto w_scale = [&](const SlabCodes<kWide>& x, const WinScales& win, int u, int64_t slab,
-                       int k, int gg) {
+                       int k, int g) {
         uint32_t b;
         if constexpr (kWide) {
-            b = (word_of(win.w[k], u) >> (qs + 8 * gg)) & 0xFFu;
+            b = (word_of(win.w[k], u) >> (qs + 8 * g)) & 0xFFu;
         } else {
-            const bool past = slab * kGroups + 2 * q + gg >= gpr;
-            b = past ? kZeroScale : x.wb[k][gg];
+            const bool past = slab * kGroups + 2 * q + g >= gpr;
+            b = past ? kZeroScale : x.wb[k][g];
         }
         return lookup_scale(smem, b);
     };
-    // W row k, group 2q + gg, half hf into `tile`
-    auto w_store = [&](const SlabCodes<kWide>& x, GroupScale sc, int k, int gg, int hf,
-                       uint8_t* tile) {
-        *reinterpret_cast<half8*>(tile + frag_off(wr_row[k], 2 * q + gg, hf)) =
-            decode_half(x.wword(k, 2 * gg + hf), sc);
+    // slabs past the end (the prefetches of the last two slabs) re-read the
+    // last slab into registers that are never decoded for use
+    auto load_codes = [&](SlabCodes<kWide>& x, int64_t slab) {
+        const int64_t sc = slab < last ? slab : last;
+        if constexpr (kWide)
+            x.load(opA, opW, sc);
+        else
+            x.load(acp, asp, wcp, wsp, sc, h, gpr);
+    };
+    // A block i, group 2h + g of codes x into a[i][2g], a[i][2g + 1]
+    half8 a[2][kGroups];  // decoded A operands [block][MFMA step] of the running slab
+    auto a_decode = [&](uint32_t w0, uint32_t w1, GroupScale sc, int i, int g) {
+        decode_group(w0, w1, sc, a[i][2 * g], a[i][2 * g + 1]);
+    };
+    // W row k, group 2q + g of codes x: both halves decoded; half 0 stored
+    // now, half 1 returned for a later store
+    auto w_decode_store0 = [&](const SlabCodes<kWide>& x, GroupScale sc, int k, int g,
+                               uint8_t* tile) {
+        half8 o0, o1;
+        decode_group(x.wword(k, 2 * g), x.wword(k, 2 * g + 1), sc, o0, o1);
+        *reinterpret_cast<half8*>(tile + frag_off(wr_row[k], 2 * q + g, 0)) = o0;
+        return o1;
+    };
+    auto w_store1 = [&](half8 o1, int k, int g, uint8_t* tile) {
+        *reinterpret_cast<half8*>(tile + frag_off(wr_row[k], 2 * q + g, 1)) = o1;
     };
 
     // register sets: raw[p] holds the codes of a slab of parity p
     SlabCodes<kWide> raw[2];
-    WinScales win[2];      // scale windows: the running one and the next
-    half8 a[2][kGroups];   // decoded A operands [block][MFMA step] of the running slab
-    uint32_t w13;          // A block 1, last step: word and scale of the running slab
-    GroupScale s13;
+    WinScales win[2];  // scale windows: the running one and the next
+    uint32_t k12, k13;  // A block 1, words 2 and 3 of the running slab, and their scale
+    GroupScale s1x;
     // Scale-table lookups run one MFMA step ahead of the decodes that use
     // them: issued before that step's fragment prefetches, a lookup can be
     // waited for (LDS operations complete in order) without waiting for the
-    // prefetches too.  la1 / la0 / lw: A block 1 (previous step's word),
-    // A block 0 and W of the coming step.
-    GroupScale la1, la0, lw;
+    // prefetches too.  la / lw: the coming step's A and W groups.
+    GroupScale la, lw;
 
-    // prologue: slab 0 decoded (W into buffer 0, A into registers), slab 1 fetched
+    // prologue: slab 0 decoded (W into buffer 0; A into registers, except
+    // block 1's words 2-3, decoded in slab 0's step 0), slab 1 fetched
     if constexpr (kWide) {
-        win[0].load(asp, wsp, 0);
-        win[1].load(asp, wsp, nwin > 1 ? 1 : 0);
+        win[0].load(opA, opW, 0);
+        win[1].load(opA, opW, nwin > 1 ? 1 : 0);
     }
-    raw[0].load(acp, asp, wcp, wsp, 0, h, q, gpr);
-    raw[1].load(acp, asp, wcp, wsp, last < 1 ? last : 1, h, q, gpr);
+    load_codes(raw[0], 0);
+    load_codes(raw[1], 1);
 #pragma unroll
-    for (int t = 0; t < kGroups; t++) {
+    for (int g = 0; g < 2; g++) {
+        a_decode(raw[0].aword(0, 2 * g), raw[0].aword(0, 2 * g + 1),
+                 a_scale(raw[0], win[0], 0, 0, 0, g), 0, g);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-            a[i][t] = decode_half(raw[0].aword(i, t), a_scale(raw[0], win[0], 0, 0, i, t));
-        const int k = t >> 1, gg = t & 1;
-        const GroupScale sw = w_scale(raw[0], win[0], 0, 0, k, gg);
-        w_store(raw[0], sw, k, gg, 0, smem);
-        w_store(raw[0], sw, k, gg, 1, smem);
+        for (int k = 0; k < 2; k++) {
+            const half8 o1 = w_decode_store0(raw[0], w_scale(raw[0], win[0], 0, 0, k, g), k, g,
+                                             smem);
+            w_store1(o1, k, g, smem);
+        }
     }
-    w13 = raw[0].aword(1, kGroups - 1);
-    s13 = a_scale(raw[0], win[0], 0, 0, 1, kGroups - 1);
-    // lookups for step 0 of slab 0, which decodes slab 1
-    la1 = s13;
-    la0 = a_scale(raw[1], win[0], 1, 1, 0, 0);
+    a_decode(raw[0].aword(1, 0), raw[0].aword(1, 1), a_scale(raw[0], win[0], 0, 0, 1, 0), 1, 0);
+    k12 = raw[0].aword(1, 2);
+    k13 = raw[0].aword(1, 3);
+    // lookups for step 0 of slab 0: A block 1 group 2h+1 of slab 0, W row 0
+    // group 2q of slab 1
+    la = a_scale(raw[0], win[0], 0, 0, 1, 1);
     lw = w_scale(raw[1], win[0], 1, 1, 0, 0);
     lds_barrier();
 
@@ -399,9 +503,6 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         const uint8_t* buf = smem + P * TILE_BYTES;
         uint8_t* nbuf = smem + Q * TILE_BYTES;
         const int64_t sn = (int64_t)s + 1;
-        // slab s+2, clamped: past the end the loads repeat the last slab and
-        // the decodes fill registers and a buffer that nobody reads again
-        const int64_t sl = (int64_t)s + 2 < last ? (int64_t)s + 2 : last;
         // scales of slab s+1: slot U+1 of this window, or slot 0 of the next;
         // of slab s+2 (looked up in the last step): slot U+2 of either
         const WinScales& sw_win = U + 1 < kWin ? wcur : wnxt;
@@ -416,20 +517,26 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 #pragma unroll
         for (int j = 0; j < 8; j++)
             bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
-        raw[P].load(acp, asp, wcp, wsp, sl, h, q, gpr);
+        load_codes(raw[P], (int64_t)s + 2);
 #pragma unroll
         for (int t = 0; t < kGroups; t++) {
             const int k = t >> 1, gg = t & 1;
-            const GroupScale sa1 = la1, sa0 = la0, sw = lw;
-            if (t + 1 < kGroups) {
-                la1 = a_scale(x, sw_win, US, sn, 1, t);
-                la0 = a_scale(x, sw_win, US, sn, 0, t + 1);
-                lw = w_scale(x, sw_win, US, sn, (t + 1) >> 1, (t + 1) & 1);
+            const GroupScale sa = la, sw = lw;
+            // lookups for step t+1's decodes (the schedule above): its A
+            // group and its W group
+            if (t == 0) {
+                la = a_scale(x, sw_win, US, sn, 0, 0);
+                lw = w_scale(x, sw_win, US, sn, 0, 1);
+            } else if (t == 1) {
+                la = a_scale(x, sw_win, US, sn, 1, 0);
+                lw = w_scale(x, sw_win, US, sn, 1, 0);
+            } else if (t == 2) {
+                la = a_scale(x, sw_win, US, sn, 0, 1);
+                lw = w_scale(x, sw_win, US, sn, 1, 1);
             } else {
-                // step 0 of the next slab: A block 1's last word of slab s+1,
-                // then A block 0 and W of slab s+2
-                la1 = a_scale(x, sw_win, US, sn, 1, kGroups - 1);
-                la0 = a_scale(raw[P], sw2_win, US2, sn + 1, 0, 0);
+                // step 0 of the next slab: A block 1 group 2h+1 of slab s+1,
+                // W row 0 group 2q of slab s+2
+                la = a_scale(x, sw_win, US, sn, 1, 1);
                 lw = w_scale(raw[P], sw2_win, US2, sn + 1, 0, 0);
             }
             // the next step's eight fragments, a whole step ahead
@@ -439,6 +546,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                     bv[(t + 1) & 1][j] = *reinterpret_cast<const half8*>(
                         buf + w_off + j * FRAG_BLOCK + (t + 1) * FRAG_STEP);
             }
+            half8 w1;
             // sub-blocks: (A block 0, W 0..3), (1, 0..3), (0, 4..7), (1, 4..7)
 #pragma unroll
             for (int sb = 0; sb < 4; sb++) {
@@ -449,29 +557,34 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][t], bv[t & 1][j],
                                                                        acc[i][j], 0, 0, 0);
                 }
-                if (sb == 0) {
-                    // t = 0: the word kept from the previous slab (sa1 holds its scale)
-                    a[1][t == 0 ? kGroups - 1 : t - 1] =
-                        decode_half(t == 0 ? w13 : x.aword(1, t - 1), sa1);
-                } else if (sb == 3) {
-                    a[0][t] = decode_half(x.aword(0, t), sa0);  // its last use was sub-block 2
-                } else {
-                    w_store(x, sw, k, gg, sb == 1 ? 0 : 1, nbuf);
+                if (sb == 0 && t == 0) {
+                    a_decode(k12, k13, sa, 1, 1);  // block 1 words 2-3 of slab s
+                } else if (sb == 0 && t == 2) {
+                    a_decode(x.aword(1, 0), x.aword(1, 1), sa, 1, 0);  // slab s+1
+                } else if (sb == 1) {
+                    w1 = w_decode_store0(x, sw, k, gg, nbuf);
+                } else if (sb == 2) {
+                    w_store1(w1, k, gg, nbuf);
+                } else if (sb == 3 && t == 1) {
+                    a_decode(x.aword(0, 0), x.aword(0, 1), sa, 0, 0);  // slab s+1
+                } else if (sb == 3 && t == 3) {
+                    a_decode(x.aword(0, 2), x.aword(0, 3), sa, 0, 1);  // slab s+1
                 }
-                // interleave: each MFMA followed by five VALU and up to two
+                // interleave: each MFMA followed by four VALU and up to two
                 // LDS reads; no fence between sub-blocks, so the scheduler
                 // may pull a later sub-block's independent work forward
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
                     if (m == 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
                     if (m == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
                 }
             }
         }
-        w13 = x.aword(1, kGroups - 1);
+        k12 = x.aword(1, 2);
+        k13 = x.aword(1, 3);
         lds_barrier();
     };
 
@@ -481,7 +594,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         WinScales nn;
         if constexpr (kWide) {
             const int64_t nw = (int64_t)s0 / kWin + 2;
-            nn.load(asp, wsp, nw < nwin ? nw : nwin - 1);
+            nn.load(opA, opW, nw < nwin ? nw : nwin - 1);
         }
         slab_step(std::integral_constant<int, 0>{}, s0, win[0], win[1]);
         if (kWide || s0 + 1 < nslabs) slab_step(std::integral_constant<int, 1>{}, s0, win[0], win[1]);
@@ -497,10 +610,10 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.  Each sum is
     // scaled by 2^out_exp with one v_ldexp_f32 (a single rounding, and only
     // where the result leaves the fp32 range: out_exp spans [-110, 146], more
-    // than one fp32 power of two can hold).  C is written
-    // with non-temporal stores: nothing here reads it again, and dirty C
-    // lines left in the caches slow whatever kernel runs next (a 470 MB
-    // quantize launched after this GEMM took 125 us instead of 101 us)
+    // than one fp32 power of two can hold).  C is written with non-temporal
+    // stores: nothing here reads it again, and dirty C lines left in the
+    // caches slow whatever kernel runs next (a 470 MB quantize launched after
+    // this GEMM took 125 us instead of 101 us)
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -557,9 +670,11 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int32_t 
     const int out_exp = a_exp + w_exp + 18;
     // Wide fetches need 16-byte aligned code and scale rows and whole 4-slab
     // scale windows.
+    // Buffer offsets are 32-bit: 257 code rows of K/2 bytes from the tile's
+    // first row must fit.
     const bool wide = K % (BK * kWin) == 0 && (uintptr_t)a_codes % 16 == 0 &&
                       (uintptr_t)w_codes % 16 == 0 && (uintptr_t)a_scales % 16 == 0 &&
-                      (uintptr_t)w_scales % 16 == 0;
+                      (uintptr_t)w_scales % 16 == 0 && (uint64_t)(BM + 1) * (K / 2) < (1ull << 31);
     return wide ? launch_tile<true>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
                                     out_exp, tiles_m, tiles_n, stream)
                 : launch_tile<false>(a_codes, a_scales, w_codes, w_scales, M, N, K, c, ldc,
