@@ -218,13 +218,19 @@ quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int
 //    e < 2^-25, so a tie a/6 = M (an E4M3 midpoint, 5 bits) rounds back to M
 //    exactly, and a bf16 a (8 bits) is never within 2^-9 relative of any other
 //    midpoint, far beyond the product's error.
-//  * codes: u = |x|/s is approximated as |x| * RN(1/s) and snapped to a 2^-18
-//    grid in the same fma (adding 48 puts the sum in [32, 64), whose fp32
-//    spacing is 2^-18).  Every midpoint of either grid is a multiple of 2^-18
-//    and the approximation error is below 2^-20, so a value exactly on a
-//    midpoint snaps onto it and every other value stays on its side (a bf16
-//    x sits at least 2^-16 from any midpoint of u or 7u/6 that it does not
-//    hit).  FP4: the snapped value carries x's sign into the hardware E2M1
+//  * codes: u = |x|/s is approximated as |x| * r, r an approximation of 1/s
+//    within 2.2 * 2^-24 relative, and snapped to a 2^-18 grid in the same fma
+//    (adding 48 puts the sum in [32, 64), whose fp32 spacing is 2^-18); 7u/6
+//    likewise with r7 ~ 7/(6s).  Every midpoint of either grid is a multiple
+//    of 2^-18, and at the largest midpoint that matters (5 for u, 6.5 for
+//    7u/6) the approximation error is below 6.5 * 2.2 * 2^-24 < 2^-20, well
+//    inside half the grid spacing, so a value exactly on a midpoint snaps onto
+//    it and every other value stays on its side (a bf16 x sits at least 2^-16
+//    from any midpoint of u or 7u/6 that it does not hit).  r is v_rcp_f32 of
+//    s' (within one ulp) refined by one Newton step (then within half an ulp
+//    plus a 2^-46 relative term), r7 = r + r * fl(1/6) in one fma; the power
+//    of two 2^-E is applied exactly after.  FP4: the snapped value carries x's
+//    sign into the hardware E2M1
 //    conversion (round to nearest even, saturating, signed zero kept), and
 //    the same hardware decodes the codes back for the error.  INT4: adding
 //    1.5 * 2^23 - 48 rounds the snapped 7|x|/(6s) to an integer (ties even),
@@ -232,25 +238,15 @@ quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int
 //  * errors: for bf16 x every d = 7x - c*7s or 7|x| - |q|*6s is exact in
 //    fp32, so fma(-c, 7s, 7x) equals the reference fma(|x|, 7, -|c|*7s).
 //  * non-finite: a NaN reaches the FP4 error sum (NaN) and an infinity the
-//    absmax; zero-scale groups use a zero reciprocal so their sums stay finite.
-// Per-workgroup table of (RN(1/s'), RN(7/(6 s'))) per scale code; 0 for
-// code 0 (and the unused NaN code), so zero-scale groups stay finite.
-__device__ __forceinline__ void fill_recip(float2* recip) {
-    if (threadIdx.x < 128) {
-        const uint32_t c = threadIdx.x;
-        float2 t = make_float2(0.0f, 0.0f);
-        if (c != 0 && c != 127) {
-            const float sp = e4m3_value(c);
-            t = make_float2(1.0f / sp, 7.0f / (6.0f * sp));
-        }
-        recip[c] = t;
-    }
-}
+//    absmax; zero-scale groups use zero reciprocals so their sums stay finite.
+// (An earlier version took r and r7 from a per-workgroup LDS table of
+// correctly rounded reciprocals; computing them per group costs fewer
+// instructions than filling the table, and drops its barrier.)
 
 // One group of bf16-exact values, fast path (see above): codes and flagged
 // scale byte, identical to exact_group for bf16 inputs.
 template <int kMode>
-__device__ __forceinline__ void fast_group(const float (&v)[16], const float2* recip,
+__device__ __forceinline__ void fast_group(const float (&v)[16],
                                            float p_exp, float p_negexp, uint32_t& lo,
                                            uint32_t& hi, uint32_t& byte) {
     float a = 0.0f;
@@ -268,9 +264,14 @@ __device__ __forceinline__ void fast_group(const float (&v)[16], const float2* r
         sc = (b >> 20) - 960u;
         sc = sc < 0x7Eu ? sc : 0x7Eu;
     }
-    const float s = e4m3_value(sc) * p_exp;
-    const float2 rc = recip[sc];
-    const float inv_s = rc.x * p_negexp, k7 = rc.y * p_negexp;
+    const float sp = e4m3_value(sc);
+    const float s = sp * p_exp;
+    float r = __builtin_amdgcn_rcpf(sp);
+    r = __builtin_fmaf(r, __builtin_fmaf(-sp, r, 1.0f), r);
+    float r7 = __builtin_fmaf(r, 0.16666667f, r);
+    r = sc != 0 ? r : 0.0f;  // (rcp(0) is infinite)
+    r7 = sc != 0 ? r7 : 0.0f;
+    const float inv_s = r * p_negexp, k7 = r7 * p_negexp;
     const float s7 = 7.0f * s, s6 = 6.0f * s;
 
     // FP4 codes via the hardware E2M1 conversion of the snapped quotients
@@ -371,7 +372,6 @@ __global__ void __launch_bounds__(kThreads)
 quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                      float p_negexp, uint32_t sign_mask) {
-    __shared__ float2 recip[128];
     // sign-bit xor words for the rotation: bf16 element 2j sits in the low
     // half of input word j, element 2j + 1 in the high half
     uint32_t flip[8];
@@ -396,12 +396,6 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
         a[k] = p[0];
         b[k] = p[1];
     }
-    // the table is built while the loads are in flight; the barrier orders
-    // LDS only (a full __syncthreads would also wait for the loads)
-    fill_recip(recip);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
     for (int k = 0; k < kGPT; k++) {
         const int64_t g = g0 + k * kThreads;
@@ -424,7 +418,7 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
             for (int i = 0; i < 16; i++) v[i] = (float)(__bf16)v[i];
         }
         uint32_t lo, hi, byte;
-        fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
+        fast_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
         if (g < ngroups) {
             *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(lo, hi);
             scales[g] = (uint8_t)byte;
@@ -480,11 +474,6 @@ __global__ void __launch_bounds__(kThreads)
 quantize_t_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                   float p_negexp, int64_t col_blocks) {
-    __shared__ float2 recip[128];
-    if constexpr (kBf16) {
-        fill_recip(recip);
-        __syncthreads();
-    }
     const int64_t cb = blockIdx.x % col_blocks, chunk = blockIdx.x / col_blocks;
     const int64_t col = cb * kThreads + threadIdx.x;
     const int64_t rgs = rows / 16;
@@ -511,7 +500,7 @@ quantize_t_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, int64_
         if (rg + 1 < rg1) load(rg + 1);
         uint32_t lo, hi, byte;
         if constexpr (kBf16)
-            fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
+            fast_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
         else
             exact_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
         *reinterpret_cast<uint2*>(codes + col * (rows / 2) + rg * 8) = make_uint2(lo, hi);
@@ -545,7 +534,6 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
     constexpr int kCodePitch = kTRG * 8 + 8;       // 64 code bytes per column
     constexpr int kScalePitch = kTRG + 4;          // 8 scale bytes per column
     __shared__ __attribute__((aligned(16))) uint8_t obuf[kTC * (kCodePitch + kScalePitch)];
-    __shared__ float2 recip[128];
 
     const int64_t ct = blockIdx.x % col_tiles, rt = blockIdx.x / col_tiles;
     const int64_t c0 = ct * kTC, r0 = rt * kTR;
@@ -600,18 +588,12 @@ quantize_t_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols, i
             vo[rr] = o;
         }
     }
-    // the reciprocal table while the loads are in flight, behind an LDS-only
-    // barrier
-    if constexpr (kBf16) fill_recip(recip);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     auto group = [&](const float* src, uint32_t& lo, uint32_t& hi, uint32_t& byte) {
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) v[i] = src[i];
         if constexpr (kBf16)
-            fast_group<kMode>(v, recip, p_exp, p_negexp, lo, hi, byte);
+            fast_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
         else
             exact_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
     };
