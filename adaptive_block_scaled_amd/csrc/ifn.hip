@@ -194,6 +194,250 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
     byte = (uint32_t)sc | (use_int ? 0x80u : 0u);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 fast path.  Same codes and scale bytes as quantize_group for every
+// bf16 input (the GPU tests sweep every (bf16 x, E4M3 s') pair for both
+// formats), with fewer instructions:
+//
+//  * quotients: u = |x|/s, and for INT the quotient on the INT grid, are
+//    approximated with reciprocals of s' (v_rcp_f32 refined by one Newton
+//    step: within 2^-24 (1 + 2^-22) relative) and snapped in the same fma to
+//    a grid that holds every midpoint exactly: u onto 2^-18 (+48, sums in
+//    [48, 64)); IF6's INT quotient 62|x|/(15 s) <= 34 onto 2^-17 (+64), as
+//    (|x| 62/64) * (64/(15 s)), the first product exact for bf16 and never
+//    overflowing; IF3's 3|x|/(4 s) = (|x| 3/4) / s <= 4 onto 2^-20 (+8).  The
+//    approximation error at the largest midpoint that matters (7.25, 30.5,
+//    2.5) stays below half the snap grid, so a value on a midpoint snaps onto
+//    it exactly, and a bf16 x that is not on a midpoint sits at least 2^-15
+//    (in quotient units) from it, far beyond the error plus half a grid step.
+//  * IF6 float codes: gfx950's E2M3 conversion (v_cvt_scalef32_2xpk16_fp6_f32,
+//    round to nearest even, saturating at 7.5, signed zero kept; checked over
+//    every multiple of 2^-18 in [-9, 9], infinities and huge values) encodes
+//    the snapped signed quotients straight into the packed 6-bit layout (it
+//    interleaves its two 16-value operands: slot 2j takes the first
+//    operand's value j, slot 2j + 1 the second's), and the matching decode
+//    (v_cvt_scalef32_pk32_f32_fp6) returns the grid values for the errors.
+//  * IF3 float codes: the snapped quotient against the three midpoints 0.5,
+//    1.5 and 3 of {0, 1, 2, 4} (> for 0.5 and 3, >= for 1.5: ties to even).
+//  * INT magnitudes: adding 1.5 * 2^23 minus the snap offset rounds the
+//    snapped quotient to an integer (ties to even) in the float's low bits;
+//    an integer min clamps it to qmax.
+//  * errors: exactly the products and fmas of the reference (c dd s and
+//    |q| dn s are exact), in index order.
+//  * non-finite: an infinity makes the absmax infinite, a NaN the float
+//    error sum NaN; zero scales get zero reciprocals so the sums stay finite.
+__device__ __forceinline__ float refined_rcp(float d) {
+    const float r = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+}
+
+template <int kBits>
+__device__ __forceinline__ int scale_code_of(float a, float p_negexp) {
+    using F = Fmt<kBits>;
+    const float ap = a * p_negexp;
+    const float qg = ap * (1.0f / F::kTop);
+    int sc = qg < 0.015625f ? (int)(qg * 512.0f) : (int)(__float_as_uint(qg) >> 20) - 960;
+    sc = sc < 126 ? sc : 126;
+    sc += passes(ap,
+                 sc < 126 ? F::kTop * (0.5f * (e4m3_value(sc) + e4m3_value(sc + 1)))
+                          : __builtin_inff(),
+                 sc);
+    return sc;
+}
+
+// the sign bit (bit 5 of each 6-bit field) positions in the three words of
+// an IF6 group's code field
+constexpr uint32_t kIf6Sign[3] = {0x20820820u, 0x08208208u, 0x82082082u};
+
+template <int kBits, int kMode>
+__device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_exp, float p_negexp,
+                                                uint32_t (&out)[3], uint32_t& byte) {
+    using F = Fmt<kBits>;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+    const int sc = scale_code_of<kBits>(a, p_negexp);
+    const float sp = e4m3_value((uint32_t)sc);
+    const float s = sp * p_exp;
+    const float sdd = F::kDd * s, sdn = F::kDn * s;  // exact
+    float r = refined_rcp(sp);
+    r = sc != 0 ? r : 0.0f;  // (rcp(0) is infinite)
+    const float rs = r * p_negexp;  // ~ 1/s
+    float ef = 0.0f, ei = 0.0f;
+    uint32_t mq[3] = {0, 0, 0};
+    auto put = [](uint32_t(&f)[3], uint32_t c, int bit) {
+        f[bit >> 5] |= c << (bit & 31);
+        if ((bit & 31) + kBits > 32) f[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+    };
+    static_assert(kBits == 3, "IF6 takes two groups at a time: if6_pair_bf16");
+    {
+        uint32_t mf[3] = {0, 0, 0}, sg[3] = {0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float ax = __builtin_fabsf(v[i]);
+            const float u = __builtin_fmaf(ax, rs, 48.0f) - 48.0f;
+            // the snapped u is a multiple of 2^-18: each step (u > 0.5,
+            // u >= 1.5, u > 3) is an fma scaled by 2^18 and clamped to [0, 1]
+            const float s1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(u, 0x1p18f, -0x1p17f), 0.0f, 1.0f);
+            const float s2 = __builtin_amdgcn_fmed3f(
+                __builtin_fmaf(u, 0x1p18f, 1.0f - 1.5f * 0x1p18f), 0.0f, 1.0f);
+            const float s3 = __builtin_amdgcn_fmed3f(__builtin_fmaf(u, 0x1p18f, -3.0f * 0x1p18f),
+                                                     0.0f, 1.0f);
+            const float s12 = s1 + s2;
+            const int fi = (int)(s12 + s3);
+            const float cv = __builtin_fmaf(2.0f, s3, s12);  // 0, 1, 2, 4
+            const float df = __builtin_fmaf(ax, F::kDd, -(cv * sdd));
+            ef = __builtin_fmaf(df, df, ef);
+            const float t = __builtin_fmaf(ax * 0.75f, rs, 8.0f);
+            const uint32_t rb =
+                __builtin_elementwise_min(__float_as_uint(t + 12582904.0f), 0x4B400003u);
+            const float q = __uint_as_float(rb) - 12582912.0f;
+            const float di = __builtin_fmaf(ax, F::kDd, -(q * sdn));
+            ei = __builtin_fmaf(di, di, ei);
+            put(mf, (uint32_t)fi, 3 * i);
+            put(mq, rb & 3u, 3 * i);
+            put(sg, (__float_as_uint(v[i]) >> 31) << 2, 3 * i);
+        }
+        const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
+#pragma unroll
+        for (int w = 0; w < 3; w++) out[w] = (use_int ? mq[w] : mf[w]) | sg[w];
+        byte = (uint32_t)sc | (use_int ? 0x80u : 0u);
+    }
+    if (sc == 0) {
+        out[0] = out[1] = out[2] = 0;
+        byte = 0;
+    }
+    if (!(a <= 3.40282347e38f) || ef != ef) {  // infinity or NaN in the group
+        out[0] = out[1] = out[2] = 0;
+        byte = 0x7Fu;
+    }
+}
+
+// IF6, two groups at a time: the E2M3 conversion takes 32 values, slot 2j
+// from its first operand's value j and slot 2j + 1 from the second's, so the
+// even elements of groups 0 and 1 go to the first operand (positions 0-7 and
+// 8-15) and the odd ones to the second, and the converted 192 bits hold group
+// 0's field in words 0-2 and group 1's in words 3-5.
+template <int kMode>
+__device__ __forceinline__ void if6_pair_bf16(const float (&v)[2][16], float p_exp,
+                                              float p_negexp, uint32_t (&out)[2][3],
+                                              uint32_t (&byte)[2]) {
+    using F = Fmt<6>;
+    typedef float v16f __attribute__((ext_vector_type(16)));
+    typedef float v32f __attribute__((ext_vector_type(32)));
+    typedef uint32_t v6u __attribute__((ext_vector_type(6)));
+    v16f ev, od;  // signed snapped quotients of the even / odd elements
+    float a[2], ei[2] = {0.0f, 0.0f}, sdd[2];
+    int sc[2];
+    uint32_t mq[2][3] = {{0, 0, 0}, {0, 0, 0}};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        a[h] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) a[h] = __builtin_fmaxf(a[h], __builtin_fabsf(v[h][i]));
+        sc[h] = scale_code_of<6>(a[h], p_negexp);
+        const float sp = e4m3_value((uint32_t)sc[h]);
+        const float s = sp * p_exp;
+        sdd[h] = F::kDd * s;
+        const float sdn = F::kDn * s;  // exact
+        float r = refined_rcp(sp), rq = refined_rcp(15.0f * sp);  // 15 s' exact
+        r = sc[h] != 0 ? r : 0.0f;  // (rcp(0) is infinite)
+        rq = sc[h] != 0 ? rq : 0.0f;
+        const float rs = r * p_negexp;          // ~ 1/s
+        rq *= 64.0f * p_negexp;                 // ~ 64 / (15 s)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float ax = __builtin_fabsf(v[h][i]);
+            const float u = __builtin_copysignf(__builtin_fmaf(ax, rs, 48.0f) - 48.0f, v[h][i]);
+            if (i & 1)
+                od[8 * h + (i >> 1)] = u;
+            else
+                ev[8 * h + (i >> 1)] = u;
+            // INT: 1.5 * 2^23 + |q| in the float's bits, |q| clamped to 31
+            const float t = __builtin_fmaf(ax * 0.96875f, rq, 64.0f);
+            const uint32_t rb =
+                __builtin_elementwise_min(__float_as_uint(t + 12582848.0f), 0x4B40001Fu);
+            const float q = __uint_as_float(rb) - 12582912.0f;
+            const float di = __builtin_fmaf(ax, F::kDd, -(q * sdn));
+            ei[h] = __builtin_fmaf(di, di, ei[h]);
+            const int bit = 6 * i;
+            const uint32_t m = rb & 31u;
+            mq[h][bit >> 5] |= m << (bit & 31);
+            if ((bit & 31) + 6 > 32) mq[h][(bit >> 5) + 1] |= m >> (32 - (bit & 31));
+        }
+    }
+    const auto fcv = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+    const v6u fc = __builtin_bit_cast(v6u, fcv);
+    const v32f c = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(fcv, 1.0f);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        float ef = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float df = __builtin_fmaf(__builtin_fabsf(v[h][i]), F::kDd,
+                                            -(__builtin_fabsf(c[16 * h + i]) * sdd[h]));
+            ef = __builtin_fmaf(df, df, ef);
+        }
+        const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei[h] < ef));
+#pragma unroll
+        for (int w = 0; w < 3; w++)
+            out[h][w] = use_int ? (mq[h][w] | (fc[3 * h + w] & kIf6Sign[w])) : fc[3 * h + w];
+        byte[h] = (uint32_t)sc[h] | (use_int ? 0x80u : 0u);
+        if (sc[h] == 0) {
+            out[h][0] = out[h][1] = out[h][2] = 0;
+            byte[h] = 0;
+        }
+        if (!(a[h] <= 3.40282347e38f) || ef != ef) {  // infinity or NaN in the group
+            out[h][0] = out[h][1] = out[h][2] = 0;
+            byte[h] = 0x7Fu;
+        }
+    }
+}
+
+// IF6 from bf16: two consecutive groups per thread (one 64-byte span of a
+// row when the row holds both), both through if6_pair_bf16
+template <int kMode, bool kContig>
+__global__ void __launch_bounds__(kThreads)
+quantize_if6_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
+                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
+                         float p_negexp) {
+    const int64_t ngroups = rows * gpr;
+    const int64_t g0 = 2 * ((int64_t)blockIdx.x * kThreads + threadIdx.x);
+    float v[2][16];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int64_t g = g0 + h < ngroups - 1 ? g0 + h : ngroups - 1;
+        int64_t off;
+        if constexpr (kContig) {
+            off = g * 16;
+        } else {
+            const int64_t r = g / gpr;
+            off = r * ld_x + (g - r * gpr) * 16;
+        }
+        const uint4* p = reinterpret_cast<const uint4*>(x + off);
+        const uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            v[h][2 * i] = __uint_as_float(w[i] << 16);
+            v[h][2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    uint32_t out[2][3], byte[2];
+    if6_pair_bf16<kMode>(v, p_exp, p_negexp, out, byte);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int64_t g = g0 + h;
+        if (g < ngroups) {
+            uint32_t* c = reinterpret_cast<uint32_t*>(codes + g * 12);
+            c[0] = out[h][0];
+            c[1] = out[h][1];
+            c[2] = out[h][2];
+            scales[g] = (uint8_t)byte[h];
+        }
+    }
+}
+
 // kContig: rows back to back (ld = cols), so a group's offset is 16 g with
 // no division by the groups per row
 template <int kBits, int kMode, bool kBf16, bool kContig>
@@ -233,7 +477,10 @@ quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64
         }
     }
     uint32_t out[3], byte;
-    quantize_group<kBits, kMode>(v, p_exp, p_negexp, out, byte);
+    if constexpr (kBf16 && kBits == 3)
+        fast_group_bf16<kBits, kMode>(v, p_exp, p_negexp, out, byte);
+    else
+        quantize_group<kBits, kMode>(v, p_exp, p_negexp, out, byte);
     if (gid >= ngroups) return;
     if constexpr (kBits == 6) {
         uint32_t* c = reinterpret_cast<uint32_t*>(codes + gid * 12);
@@ -363,6 +610,20 @@ template <int kBits, int kMode, bool kBf16>
 hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                     uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
     const int64_t gpr = cols / 16;
+    if constexpr (kBits == 6 && kBf16) {
+        const int64_t blocks = (rows * gpr + 2 * kThreads - 1) / (2 * kThreads);
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+        if (ld_x == cols)
+            hipLaunchKernelGGL((quantize_if6_bf16_kernel<kMode, true>), dim3((unsigned)blocks),
+                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales,
+                               pow2f(scale_exp), pow2f(-scale_exp));
+        else
+            hipLaunchKernelGGL((quantize_if6_bf16_kernel<kMode, false>), dim3((unsigned)blocks),
+                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales,
+                               pow2f(scale_exp), pow2f(-scale_exp));
+        return hipGetLastError();
+    }
     const int64_t blocks = (rows * gpr + kThreads - 1) / kThreads;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (ld_x == cols)

@@ -210,3 +210,39 @@ def test_full_size_weight_sampled(oracle_mod):
         want = torch.from_numpy(oracle_mod.dequantize_ifn(oc, os_, bits, t.scale_exp))
         assert torch.equal(y[idx].cpu(), want.to(torch.bfloat16)), bits
         del c, s, y
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_exhaustive_bf16_element_codes(oracle_mod, bits):
+    """Every (bf16 |x| <= top s', E4M3 scale s') pair, both signs: groups
+    [top s', x, ...] pin the scale at s', so each element's float and INT
+    codes and both error sums are exercised for every representable bf16
+    input (the bf16 kernel's snapped-quotient roundings against the oracle's
+    exact ones), at E = 0 and, shifted, at E = 7 and E = -30."""
+    top = 7.5 if bits == 6 else 4.0
+    positive = np.arange(0, 0x7F80, dtype=np.uint32) << 16
+    positive = positive.view(np.float32)
+    rows = []
+    for sc in range(1, 127):
+        e, m = sc >> 3, sc & 7
+        sp = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        xs = positive[positive <= top * sp * 1.0625]
+        vals = np.concatenate([xs, -xs])
+        pad = (-vals.size) % 15
+        vals = np.concatenate([vals, np.zeros(pad, np.float32)]).reshape(-1, 15)
+        grp = np.empty((vals.shape[0], 16), np.float32)
+        grp[:, 0] = np.float32(top * sp)
+        grp[:, 1:] = vals
+        rows.append(grp)
+    allg = np.concatenate(rows)
+    pad = (-allg.shape[0]) % 64
+    allg = np.concatenate([allg, np.zeros((pad, 16), np.float32)])
+    x = allg.reshape(-1, 64 * 16)
+    assert np.array_equal(wl.to_bf16_f32(x), x)
+    print(f"[ifn] exhaustive bf16 sweep IF{bits}: {allg.shape[0]} groups", flush=True)
+    for e in (0, 7, -30):
+        # (the shift down by 2^30 rounds the smallest values to bf16 again)
+        xe = wl.to_bf16_f32(np.ldexp(x, e).astype(np.float32))
+        c, s_ = check_q(oracle_mod, xe, bits, "bf16", e, label=f"exhaustive E={e}")
+        sc_seen = np.unique(s_.cpu().numpy() & 0x7F)
+        assert sc_seen.size >= 126
