@@ -349,6 +349,35 @@ def mean_launch_ms(torch, calls, n=100, warmup=200, batches=3):
     return sorted(per)[batches // 2]
 
 
+def graph_launch_ms(torch, dev, *calls, n=100, replays=5):
+    """GPU time per launch of each call (a function of the stream handle):
+    n launches captured in one HIP graph, replayed between HIP events; the
+    median over `replays` replays.  The calls must launch plain kernels only
+    (no memset or host work), which holds for every entry point here."""
+    out = []
+    for call in calls:
+        s = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            call(s.cuda_stream)  # warm-up outside the graph
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(n):
+                    st = call(torch.cuda.current_stream(dev).cuda_stream)
+                    assert st == 0, st
+        per = []
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+        out.append(sorted(per)[replays // 2])
+        del g
+    return out
+
+
 def time_other_configs(torch, if4, wl, dev, min_bytes=512 << 20):
     """The smaller workloads at their own shapes: the C2 activation and C3
     gradient quantizes (C3 also through the fused rotate-and-quantize from
@@ -404,17 +433,28 @@ def time_other_configs(torch, if4, wl, dev, min_bytes=512 << 20):
                 "copy_same_bytes_GB/s": round(byts / (cms * 1e-3) / 1e9, 1),
                 "frac_of_copy": round(cms / ms, 4)}
 
-    # C1: fp32 256x256 through the exact kernel, and back to fp32 (tiny:
-    # the launch dominates; reported in microseconds)
+    # C1: fp32 256x256 through the exact kernel, and back to fp32.  Tiny
+    # kernels: 100 launches through the C ABI are captured in a HIP graph and
+    # replayed, so the time per launch is the GPU's, not the host's call and
+    # launch overhead (reported in microseconds)
     t = wl.c1_mixed_fp32()
     x1 = torch.from_numpy(t.values).to(dev)
     c1, s1 = if4.quantize(x1, t.scale_exp)
-    y1 = torch.empty_like(x1)
-    ms_q = mean_launch_ms(torch, [lambda: if4.quantize(x1, t.scale_exp, out=(c1, s1))])
-    ms_d = mean_launch_ms(torch, [lambda: if4.dequantize(c1, s1, t.scale_exp, torch.float32, out=y1)])
-    out["C1_fp32_quantize_dequantize"] = {"shape": list(t.values.shape), "E": t.scale_exp,
-                                          "quantize_us": round(ms_q * 1e3, 2),
-                                          "dequantize_us": round(ms_d * 1e3, 2)}
+    y1 = if4.dequantize(c1, s1, t.scale_exp, torch.float32)
+    torch.cuda.synchronize()
+    c1_ref, s1_ref, y1_ref = c1.clone(), s1.clone(), y1.clone()
+    R1, C1 = t.values.shape
+    q_ms, d_ms = graph_launch_ms(
+        torch, dev,
+        lambda st: if4.lib.if4_quantize_mode(x1.data_ptr(), 0, R1, C1, C1, c1.data_ptr(),
+                                             s1.data_ptr(), t.scale_exp, 0, st),
+        lambda st: if4.lib.if4_dequantize(c1.data_ptr(), s1.data_ptr(), R1, C1, t.scale_exp,
+                                          y1.data_ptr(), 0, C1, st))
+    assert torch.equal(c1, c1_ref) and torch.equal(s1, s1_ref) and torch.equal(y1, y1_ref)
+    out["C1_fp32_quantize_dequantize"] = {"shape": [R1, C1], "E": t.scale_exp,
+                                          "quantize_us": round(q_ms * 1e3, 2),
+                                          "dequantize_us": round(d_ms * 1e3, 2),
+                                          "timing": "graph replay of 100 C-ABI launches"}
     del x1, c1, s1, y1
 
     t = wl.c2_activations()

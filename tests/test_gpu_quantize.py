@@ -216,3 +216,29 @@ def test_full_size_configs(oracle_mod, cfg):
             assert frac_zero > 0.99  # sigma = 1e-3 underflows the E4M3 scale at E = 0
         else:
             assert frac_zero < 0.01
+
+
+def test_fp32_grid_stride_beyond_one_pass(oracle_mod):
+    """The fp32 kernel caps its grid at 65536 workgroups of 256 groups
+    (16,777,216 groups) and strides over the rest.  A 4096 x 65600 fp32
+    tensor has 16,793,600 groups: every group from row 4092, column-group 16
+    on is quantized by the loop's second pass.  The input is drawn on the GPU
+    (seeded), and rows on both sides of that boundary, plus the first row,
+    are checked against the oracle in full."""
+    if4 = _if4()
+    rows, cols = 4096, 65600
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.randn((rows, cols), generator=gen, device="cuda", dtype=torch.float32)
+    x[4094] *= 1e-3  # a row at a different exponent
+    e = 0
+    print(f"[quantize] fp32 grid stride rows={rows} cols={cols} groups={rows * cols // 16}",
+          flush=True)
+    codes, scales = if4.quantize(x, e)
+    torch.cuda.synchronize()
+    sample = [0, 2047, 4091, 4092, 4093, 4094, 4095]
+    assert rows * (cols // 16) > 65536 * 256 > 4092 * (cols // 16)
+    xs = x[sample].cpu().numpy()
+    oc, os_ = oracle_mod.quantize(xs, e)
+    gc, gs = codes[sample].cpu().numpy(), scales[sample].cpu().numpy()
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, oc)
