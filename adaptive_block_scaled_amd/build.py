@@ -9,6 +9,12 @@ Flags:
                                 IEEE fp32 (denormals kept, exact division).
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                 no packed fp32 (v_pk_*_f32) code generation.
+
+`python -m adaptive_block_scaled_amd.build --sanitize` also builds
+libif4_san.so: the host-only C-ABI front end (argument validation) compiled by
+the ROCm toolchain's clang++ with AddressSanitizer and UndefinedBehaviorSanitizer,
+linked with the same kernel objects.  The binding loads it when IF4_LIB names
+it; the sanitizer runtime must be preloaded (the command is in the design doc).
 """
 import os
 import subprocess
@@ -18,6 +24,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libif4.so")
+SAN_LIB = os.path.join(HERE, "libif4_san.so")
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
 
 SOURCES = ["api.cpp", "quantize.hip", "dequantize.hip", "gemm.hip", "ifn.hip"]
 
@@ -72,5 +80,34 @@ def _wait(item):
         sys.stderr.write("\n".join(lines) + "\n")
 
 
+def build_sanitized_front_end(verbose: bool = False) -> str:
+    """api.cpp (host code only) with ASan + UBSan, linked with the kernel
+    objects of the last build()."""
+    objdir = os.path.join(HERE, "_build")
+    kernels = [os.path.join(objdir, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        build(verbose=verbose)
+    api_obj = os.path.join(objdir, "api_san.o")
+    cmd = [CLANGXX, "-O1", "-g", "-std=c++17", "-fPIC", "-fno-omit-frame-pointer",
+           "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-o", SAN_LIB + ".tmp", api_obj] + kernels
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized_front_end(verbose=True))
+    else:
+        print(build(verbose=True))

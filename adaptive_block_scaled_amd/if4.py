@@ -12,7 +12,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libif4.so")
+# IF4_LIB selects another build of the same sources (the sanitizer build)
+LIB_PATH = os.environ.get("IF4_LIB") or os.path.join(HERE, "libif4.so")
 
 IF4_OK, IF4_ERR_NULL, IF4_ERR_SHAPE, IF4_ERR_ALIGN, IF4_ERR_DTYPE, IF4_ERR_RANGE, IF4_ERR_HIP = range(7)
 IF4_F32, IF4_BF16 = 0, 1
