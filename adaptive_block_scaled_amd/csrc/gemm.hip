@@ -455,8 +455,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // register sets: raw[p] holds the codes of a slab of parity p
     SlabCodes<kWide> raw[2];
     WinScales win[2];  // scale windows: the running one and the next
-    uint32_t k12, k13;  // A block 1, words 2 and 3 of the running slab, and their scale
-    GroupScale s1x;
+    uint32_t k12, k13;  // A block 1, words 2 and 3 of the running slab
     // Scale-table lookups run one MFMA step ahead of the decodes that use
     // them: issued before that step's fragment prefetches, a lookup can be
     // waited for (LDS operations complete in order) without waiting for the

@@ -355,20 +355,22 @@ __device__ __forceinline__ void fast_group(const float (&v)[16],
     }
 }
 
-// The bf16 kernel is one-shot: each thread quantizes kGPT groups, kThreads
+// The bf16 kernel is one-shot: each thread quantizes kGPT groups, kRowThreads
 // apart (a wave's loads stay contiguous: 64 lanes x 32 bytes), with all of its
 // loads issued before the first group is quantized, and one workgroup per
-// kThreads * kGPT groups.  Past the end a load re-reads the last group and
+// kRowThreads * kGPT groups.  Past the end a load re-reads the last group and
 // its store is skipped, so no load sits behind a branch.  One group per
 // thread: on the 470 MB weight one, two and four groups per thread run alike,
 // and on 86-172 MB tensors one is 4-9% faster (more, smaller workgroups fill
-// the chip sooner and leave a shorter tail).  (A grid-stride loop over fewer
-// workgroups, with the next group prefetched into a second register set,
+// the chip sooner and leave a shorter tail); for the same reason workgroups of
+// two waves run 1-2% faster than four or eight.  (A grid-stride loop over
+// fewer workgroups, with the next group prefetched into a second register set,
 // measured 8-11% slower on the weight.)
+constexpr int kRowThreads = 128;
 constexpr int kGPT = 1;
 
 template <int kMode, bool kContig, bool kRotate>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kRowThreads)
 quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                      float p_negexp, uint32_t sign_mask) {
@@ -379,11 +381,11 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
     for (int j = 0; j < 8; j++)
         flip[j] = (((sign_mask >> (2 * j)) & 1u) << 15) | (((sign_mask >> (2 * j + 1)) & 1u) << 31);
     const int64_t ngroups = rows * gpr, last = ngroups - 1;
-    const int64_t g0 = (int64_t)blockIdx.x * (kThreads * kGPT) + threadIdx.x;
+    const int64_t g0 = (int64_t)blockIdx.x * (kRowThreads * kGPT) + threadIdx.x;
     uint4 a[kGPT], b[kGPT];
 #pragma unroll
     for (int k = 0; k < kGPT; k++) {
-        int64_t g = g0 + k * kThreads;
+        int64_t g = g0 + k * kRowThreads;
         g = g < last ? g : last;
         int64_t off;
         if constexpr (kContig) {
@@ -398,7 +400,7 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
     }
 #pragma unroll
     for (int k = 0; k < kGPT; k++) {
-        const int64_t g = g0 + k * kThreads;
+        const int64_t g = g0 + k * kRowThreads;
         uint32_t w[8] = {a[k].x, a[k].y, a[k].z, a[k].w, b[k].x, b[k].y, b[k].z, b[k].w};
         if constexpr (kRotate) {
 #pragma unroll
@@ -433,16 +435,16 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
     const int64_t ngroups = rows * gpr;
     const float pe = pow2f(scale_exp), pn = pow2f(-scale_exp);
     if constexpr (kBf16) {
-        const int64_t blocks = (ngroups + kThreads * kGPT - 1) / (kThreads * kGPT);
+        const int64_t blocks = (ngroups + kRowThreads * kGPT - 1) / (kRowThreads * kGPT);
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
         const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
         if (ld_x == cols)
             hipLaunchKernelGGL((quantize_bf16_kernel<kMode, true, kRotate>),
-                               dim3((unsigned)blocks), dim3(kThreads), 0, stream, xb, rows, gpr,
+                               dim3((unsigned)blocks), dim3(kRowThreads), 0, stream, xb, rows, gpr,
                                ld_x, codes, scales, pe, pn, sign_mask);
         else
             hipLaunchKernelGGL((quantize_bf16_kernel<kMode, false, kRotate>),
-                               dim3((unsigned)blocks), dim3(kThreads), 0, stream, xb, rows, gpr,
+                               dim3((unsigned)blocks), dim3(kRowThreads), 0, stream, xb, rows, gpr,
                                ld_x, codes, scales, pe, pn, sign_mask);
     } else {
         // the exact kernel: one group per thread where the grid allows
