@@ -613,6 +613,9 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // stores: nothing here reads it again, and dirty C lines left in the
     // caches slow whatever kernel runs next (a 470 MB quantize launched after
     // this GEMM took 125 us instead of 101 us)
+    // (the lane half recomputed from the lane id, so that nothing computed
+    // before the K loop has to stay live across it)
+    const int eh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -620,7 +623,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
             const int64_t col = n0 + j * 32 + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * eh + (r & 3);
                 if (row < M && col < N)
                     __builtin_nontemporal_store(__builtin_amdgcn_ldexpf(acc[i][j][r], out_exp),
                                                 &c[row * ldc + col]);

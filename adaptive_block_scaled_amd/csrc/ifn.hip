@@ -205,7 +205,8 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 //    a grid that holds every midpoint exactly: u onto 2^-18 (+48, sums in
 //    [48, 64)); IF6's INT quotient 62|x|/(15 s) <= 34 onto 2^-17 (+64), as
 //    (|x| 62/64) * (64/(15 s)), the first product exact for bf16 and never
-//    overflowing; IF3's 3|x|/(4 s) = (|x| 3/4) / s <= 4 onto 2^-20 (+8).  The
+//    overflowing; IF3's 3|x|/(4 s) onto 2^-19 (+16), as |x| * fl(0.75 r)
+//    (one more rounding: within 2^-23 (1 + 2^-22) relative).  The
 //    approximation error at the largest midpoint that matters (7.25, 30.5,
 //    2.5) stays below half the snap grid, so a value on a midpoint snaps onto
 //    it exactly, and a bf16 x that is not on a midpoint sits at least 2^-15
@@ -218,12 +219,14 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 //    operand's value j, slot 2j + 1 the second's), and the matching decode
 //    (v_cvt_scalef32_pk32_f32_fp6) returns the grid values for the errors.
 //  * IF3 float codes: the snapped quotient against the three midpoints 0.5,
-//    1.5 and 3 of {0, 1, 2, 4} (> for 0.5 and 3, >= for 1.5: ties to even).
+//    1.5 and 3 of {0, 1, 2, 4} (> for 0.5 and 3, >= for 1.5: ties to even),
+//    each as one fma of the snapped sum (48 not subtracted) clamped to [0, 1].
 //  * INT magnitudes: adding 1.5 * 2^23 minus the snap offset rounds the
 //    snapped quotient to an integer (ties to even) in the float's low bits;
 //    an integer min clamps it to qmax.
 //  * errors: exactly the products and fmas of the reference (c dd s and
-//    |q| dn s are exact), in index order.
+//    |q| dn s are exact), in index order; IF3 subtracts them from dd |x|
+//    computed once (exact for bf16), which rounds the same difference once.
 //  * non-finite: an infinity makes the absmax infinite, a NaN the float
 //    error sum NaN; zero scales get zero reciprocals so the sums stay finite.
 __device__ __forceinline__ float refined_rcp(float d) {
@@ -262,7 +265,8 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_ex
     const float sdd = F::kDd * s, sdn = F::kDn * s;  // exact
     float r = refined_rcp(sp);
     r = sc != 0 ? r : 0.0f;  // (rcp(0) is infinite)
-    const float rs = r * p_negexp;  // ~ 1/s
+    const float rs = r * p_negexp;                // ~ 1/s
+    const float rs34 = (0.75f * r) * p_negexp;    // ~ 3/(4s), one more rounding
     float ef = 0.0f, ei = 0.0f;
     uint32_t mq[3] = {0, 0, 0};
     auto put = [](uint32_t(&f)[3], uint32_t c, int bit) {
@@ -275,24 +279,31 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_ex
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const float ax = __builtin_fabsf(v[i]);
-            const float u = __builtin_fmaf(ax, rs, 48.0f) - 48.0f;
-            // the snapped u is a multiple of 2^-18: each step (u > 0.5,
-            // u >= 1.5, u > 3) is an fma scaled by 2^18 and clamped to [0, 1]
-            const float s1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(u, 0x1p18f, -0x1p17f), 0.0f, 1.0f);
+            // 3|x|, exact for bf16 (where it overflows, so does the reference's
+            // fused 3|x| - c s dd, whose subtrahend is far below an ulp there)
+            const float x3 = ax * F::kDd;
+            // u + 48, u = |x|/s snapped to a multiple of 2^-18 (sums in [48, 64));
+            // each step (u > 0.5, u >= 1.5, u > 3) is an fma of the snapped sum
+            // scaled by 2^18 -- an exact integer -- clamped to [0, 1]
+            const float u48 = __builtin_fmaf(ax, rs, 48.0f);
+            const float s1 = __builtin_amdgcn_fmed3f(
+                __builtin_fmaf(u48, 0x1p18f, -48.5f * 0x1p18f), 0.0f, 1.0f);
             const float s2 = __builtin_amdgcn_fmed3f(
-                __builtin_fmaf(u, 0x1p18f, 1.0f - 1.5f * 0x1p18f), 0.0f, 1.0f);
-            const float s3 = __builtin_amdgcn_fmed3f(__builtin_fmaf(u, 0x1p18f, -3.0f * 0x1p18f),
-                                                     0.0f, 1.0f);
+                __builtin_fmaf(u48, 0x1p18f, 1.0f - 49.5f * 0x1p18f), 0.0f, 1.0f);
+            const float s3 = __builtin_amdgcn_fmed3f(
+                __builtin_fmaf(u48, 0x1p18f, -51.0f * 0x1p18f), 0.0f, 1.0f);
             const float s12 = s1 + s2;
             const int fi = (int)(s12 + s3);
             const float cv = __builtin_fmaf(2.0f, s3, s12);  // 0, 1, 2, 4
-            const float df = __builtin_fmaf(ax, F::kDd, -(cv * sdd));
+            const float df = __builtin_fmaf(-cv, sdd, x3);
             ef = __builtin_fmaf(df, df, ef);
-            const float t = __builtin_fmaf(ax * 0.75f, rs, 8.0f);
+            // 3|x|/(4s) snapped to a multiple of 2^-19 (sums in [16, 32)); 1.5 *
+            // 2^23 - 16 more rounds it to an integer (ties even) in the low bits
+            const float t = __builtin_fmaf(ax, rs34, 16.0f);
             const uint32_t rb =
-                __builtin_elementwise_min(__float_as_uint(t + 12582904.0f), 0x4B400003u);
+                __builtin_elementwise_min(__float_as_uint(t + 12582896.0f), 0x4B400003u);
             const float q = __uint_as_float(rb) - 12582912.0f;
-            const float di = __builtin_fmaf(ax, F::kDd, -(q * sdn));
+            const float di = __builtin_fmaf(-q, sdn, x3);
             ei = __builtin_fmaf(di, di, ei);
             put(mf, (uint32_t)fi, 3 * i);
             put(mq, rb & 3u, 3 * i);
