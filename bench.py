@@ -157,22 +157,10 @@ def main():
     # dequantize of W's codes to bf16, timed on its own after the step loop;
     # its 587 MB working set exceeds the 256 MB last-level cache, so repeated
     # launches stream from HBM (A's 168 MB would partly stay cached)
-    ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(2):
-        if4.dequantize(wc, ws, ew, torch.bfloat16, out=Y)
-    ev_d[0].record()
-    nd = 10
-    for _ in range(nd):
-        if4.dequantize(wc, ws, ew, torch.bfloat16, out=Y)
-    ev_d[1].record()
-    torch.cuda.synchronize()
-    ms_deq = ev_d[0].elapsed_time(ev_d[1]) / nd
-
-    # the widened rows, timed the same way on W (beyond the last-level cache):
-    # quantize of W^T (groups along dim 0, the backward products' layout) and
-    # the random-sign Hadamard rotation fused into the quantize
-    def time_launches(fn, n=10):
-        for _ in range(2):
+    # (8 warm-up launches: the clock settles over the first few launches of a
+    # kernel that follows a different one)
+    def time_launches(fn, n=20):
+        for _ in range(8):
             fn()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
@@ -181,6 +169,12 @@ def main():
         ev[1].record()
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / n
+
+    ms_deq = time_launches(lambda: if4.dequantize(wc, ws, ew, torch.bfloat16, out=Y))
+
+    # the widened rows, timed the same way on W (beyond the last-level cache):
+    # quantize of W^T (groups along dim 0, the backward products' layout) and
+    # the random-sign Hadamard rotation fused into the quantize
 
     # the W quantize again, back to back on its own (in the step it follows
     # the GEMM, whose 940 MB of output is still being written back)
@@ -207,16 +201,8 @@ def main():
     # practical HBM reference: a plain device-to-device copy of W's bf16 input
     # (reads and writes the same number of bytes), timed like the kernels
     Wc = torch.empty_like(W)
-    for _ in range(2):
-        Wc.copy_(W)
-    ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev_c[0].record()
-    for _ in range(nd):
-        Wc.copy_(W)
-    ev_c[1].record()
-    torch.cuda.synchronize()
     copy_bytes = 2 * W.numel() * W.element_size()
-    copy_gbs = copy_bytes / (ev_c[0].elapsed_time(ev_c[1]) / nd * 1e-3) / 1e9
+    copy_gbs = copy_bytes / (time_launches(lambda: Wc.copy_(W)) * 1e-3) / 1e9
     del Wc
 
     # practical MFMA reference: the vendor library's dense fp16 GEMM of the
