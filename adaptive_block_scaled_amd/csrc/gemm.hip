@@ -108,26 +108,20 @@ __device__ __forceinline__ GroupScale lookup_scale(const uint8_t* smem, uint32_t
 __device__ __forceinline__ uint32_t bit_select(uint32_t a, uint32_t b, uint32_t m) {
     return __builtin_amdgcn_bitop3_b32(a, b, m, 0xE4);
 }
-// 64-bit shifts by 4 as single instructions (full rate on gfx950; the
-// compiler otherwise splits them into two 32-bit operations).
-__device__ __forceinline__ uint64_t shr64_by4(uint64_t x) {
-    uint64_t r;
-    asm("v_lshrrev_b64 %0, 4, %1" : "=v"(r) : "v"(x));
-    return r;
-}
-__device__ __forceinline__ uint64_t shl64_by4(uint64_t x) {
-    uint64_t r;
-    asm("v_lshlrev_b64 %0, 4, %1" : "=v"(r) : "v"(x));
-    return r;
-}
+// 64-bit shifts by 4 as single instructions (full rate on gfx950).  The
+// amount comes in as `four`, a value the compiler cannot fold: a constant
+// amount makes it split each shift into two 32-bit operations, and writing the
+// instruction as inline asm instead costs a hazard s_nop after every one.
+__device__ __forceinline__ uint64_t shr64_by4(uint64_t x, uint32_t four) { return x >> four; }
+__device__ __forceinline__ uint64_t shl64_by4(uint64_t x, uint32_t four) { return x << four; }
 __device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, GroupScale s, half8& o0,
-                                             half8& o1) {
+                                             half8& o1, uint32_t four) {
     constexpr uint32_t kLo = 0x0F0F0F0Fu;  // low nibble of every byte
     const uint32_t m0 = w0 & 0x77777777u, m1 = w1 & 0x77777777u;
     const uint64_t ms = ((uint64_t)m1 << 32 | m0) << s.sh;
-    const uint64_t mr = shr64_by4(ms);
+    const uint64_t mr = shr64_by4(ms, four);
     const uint32_t g0 = w0 ^ m0, g1 = w1 ^ m1;  // sign bits (bits 3 and 7 of each byte)
-    const uint64_t g4 = shl64_by4((uint64_t)g1 << 32 | g0);
+    const uint64_t g4 = shl64_by4((uint64_t)g1 << 32 | g0, four);
     const uint32_t he0 = bit_select((uint32_t)ms, (uint32_t)g4, kLo);
     const uint32_t he1 = bit_select((uint32_t)(ms >> 32), (uint32_t)(g4 >> 32), kLo);
     const uint32_t ho0 = bit_select((uint32_t)mr, g0, kLo);
@@ -333,6 +327,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     const int tm = first_m + in_band % band_m, tn = in_band / band_m;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t kb = K / 2, gpr = K / 16;
+    const uint32_t four = 4u + (uint32_t)((uint64_t)K >> 63);  // 4 (K > 0), not foldable
 
     // rows of this lane: A rows 64w + 32i + lane%32 of the tile (i = 0, 1),
     // W rows 64w + 32k + lane%32 (k = 0, 1); K-half h = q = lane/32
@@ -437,14 +432,14 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // A block i, group 2h + g of codes x into a[i][2g], a[i][2g + 1]
     half8 a[2][kGroups];  // decoded A operands [block][MFMA step] of the running slab
     auto a_decode = [&](uint32_t w0, uint32_t w1, GroupScale sc, int i, int g) {
-        decode_group(w0, w1, sc, a[i][2 * g], a[i][2 * g + 1]);
+        decode_group(w0, w1, sc, a[i][2 * g], a[i][2 * g + 1], four);
     };
     // W row k, group 2q + g of codes x: both halves decoded; half 0 stored
     // now, half 1 returned for a later store
     auto w_decode_store0 = [&](const SlabCodes<kWide>& x, GroupScale sc, int k, int g,
                                uint8_t* tile) {
         half8 o0, o1;
-        decode_group(x.wword(k, 2 * g), x.wword(k, 2 * g + 1), sc, o0, o1);
+        decode_group(x.wword(k, 2 * g), x.wword(k, 2 * g + 1), sc, o0, o1, four);
         *reinterpret_cast<half8*>(tile + frag_off(wr_row[k], 2 * q + g, 0)) = o0;
         return o1;
     };
