@@ -363,10 +363,10 @@ __device__ __forceinline__ void fast_group(const float (&v)[16],
 // thread: on the 470 MB weight one, two and four groups per thread run alike,
 // and on 86-172 MB tensors one is 4-9% faster (more, smaller workgroups fill
 // the chip sooner and leave a shorter tail); for the same reason workgroups of
-// two waves run 1-2% faster than four or eight.  (A grid-stride loop over
-// fewer workgroups, with the next group prefetched into a second register set,
-// measured 8-11% slower on the weight.)
-constexpr int kRowThreads = 128;
+// one wave run faster than two (1.5-4%) and two faster than four or eight
+// (1-2%).  (A grid-stride loop over fewer workgroups, with the next group
+// prefetched into a second register set, measured 8-11% slower on the weight.)
+constexpr int kRowThreads = 64;
 constexpr int kGPT = 1;
 
 template <int kMode, bool kContig, bool kRotate>
