@@ -16,8 +16,9 @@
 // Element i of a group occupies bits [bits*i, bits*(i+1)) of the group's
 // little-endian 2*bits-byte code field.
 //
-// One group per thread, one workgroup per 256 groups, the thread's loads
-// issued first.  Every rounding is decided exactly (exact comparisons, or the
+// One group per thread (IF6 from bf16: two), one-wave workgroups for the
+// quantizes and 256-thread ones for the dequantize, the thread's loads issued
+// first.  Every rounding is decided exactly (exact comparisons, or the
 // exact sign of one fma), ties to the even index -- valid for any fp32 input
 // -- in branch-free code.
 #include <hip/hip_runtime.h>
@@ -28,7 +29,8 @@
 namespace if4 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // dequantize: one workgroup builds its LDS tables for 256 groups
+constexpr int kQThreads = 64;  // quantizes (no LDS): one-wave workgroups fill the chip sooner
 
 template <int kBits>
 struct Fmt;
@@ -275,7 +277,7 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_ex
     };
     static_assert(kBits == 3, "IF6 takes two groups at a time: if6_pair_bf16");
     {
-        uint32_t mf[3] = {0, 0, 0}, sg[3] = {0, 0, 0};
+        uint32_t fiv[16], qv[16], sv[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const float ax = __builtin_fabsf(v[i]);
@@ -305,13 +307,16 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_ex
             const float q = __uint_as_float(rb) - 12582912.0f;
             const float di = __builtin_fmaf(-q, sdn, x3);
             ei = __builtin_fmaf(di, di, ei);
-            put(mf, (uint32_t)fi, 3 * i);
-            put(mq, rb & 3u, 3 * i);
-            put(sg, (__float_as_uint(v[i]) >> 31) << 2, 3 * i);
+            fiv[i] = (uint32_t)fi;
+            qv[i] = rb & 3u;
+            sv[i] = __float_as_uint(v[i]) >> 31;
         }
         const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
+        // the chosen format's codes, packed once
 #pragma unroll
-        for (int w = 0; w < 3; w++) out[w] = (use_int ? mq[w] : mf[w]) | sg[w];
+        for (int i = 0; i < 16; i++) put(mq, (use_int ? qv[i] : fiv[i]) | (sv[i] << 2), 3 * i);
+#pragma unroll
+        for (int w = 0; w < 3; w++) out[w] = mq[w];
         byte = (uint32_t)sc | (use_int ? 0x80u : 0u);
     }
     if (sc == 0) {
@@ -408,12 +413,12 @@ __device__ __forceinline__ void if6_pair_bf16(const float (&v)[2][16], float p_e
 // IF6 from bf16: two consecutive groups per thread (one 64-byte span of a
 // row when the row holds both), both through if6_pair_bf16
 template <int kMode, bool kContig>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kQThreads)
 quantize_if6_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                          float p_negexp) {
     const int64_t ngroups = rows * gpr;
-    const int64_t g0 = 2 * ((int64_t)blockIdx.x * kThreads + threadIdx.x);
+    const int64_t g0 = 2 * ((int64_t)blockIdx.x * kQThreads + threadIdx.x);
     float v[2][16];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
@@ -452,12 +457,12 @@ quantize_if6_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t g
 // kContig: rows back to back (ld = cols), so a group's offset is 16 g with
 // no division by the groups per row
 template <int kBits, int kMode, bool kBf16, bool kContig>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kQThreads)
 quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                     float p_negexp) {
     const int64_t ngroups = rows * gpr;
-    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t gid = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
     const int64_t g = gid < ngroups - 1 ? gid : ngroups - 1;
     int64_t off;
     if constexpr (kContig) {
@@ -622,28 +627,28 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uin
                     uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
     const int64_t gpr = cols / 16;
     if constexpr (kBits == 6 && kBf16) {
-        const int64_t blocks = (rows * gpr + 2 * kThreads - 1) / (2 * kThreads);
+        const int64_t blocks = (rows * gpr + 2 * kQThreads - 1) / (2 * kQThreads);
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
         const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
         if (ld_x == cols)
             hipLaunchKernelGGL((quantize_if6_bf16_kernel<kMode, true>), dim3((unsigned)blocks),
-                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales,
+                               dim3(kQThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales,
                                pow2f(scale_exp), pow2f(-scale_exp));
         else
             hipLaunchKernelGGL((quantize_if6_bf16_kernel<kMode, false>), dim3((unsigned)blocks),
-                               dim3(kThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales,
+                               dim3(kQThreads), 0, stream, xb, rows, gpr, ld_x, codes, scales,
                                pow2f(scale_exp), pow2f(-scale_exp));
         return hipGetLastError();
     }
-    const int64_t blocks = (rows * gpr + kThreads - 1) / kThreads;
+    const int64_t blocks = (rows * gpr + kQThreads - 1) / kQThreads;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (ld_x == cols)
         hipLaunchKernelGGL((quantize_ifn_kernel<kBits, kMode, kBf16, true>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales,
+                           dim3(kQThreads), 0, stream, x, rows, gpr, ld_x, codes, scales,
                            pow2f(scale_exp), pow2f(-scale_exp));
     else
         hipLaunchKernelGGL((quantize_ifn_kernel<kBits, kMode, kBf16, false>),
-                           dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, rows, gpr, ld_x,
+                           dim3((unsigned)blocks), dim3(kQThreads), 0, stream, x, rows, gpr, ld_x,
                            codes, scales, pow2f(scale_exp), pow2f(-scale_exp));
     return hipGetLastError();
 }
