@@ -179,15 +179,18 @@ __device__ __forceinline__ void hadamard16(float (&v)[16]) {
 }
 
 // ---------------------------------------------------------------------------
-// Exact reference path (any fp32 input): thresholds compared exactly.
+// Exact reference path (any fp32 input): thresholds compared exactly.  One-wave
+// workgroups, as for the bf16 kernel: a small tensor (the 256x256 one holds
+// 4096 groups) then spreads over 64 CUs instead of 16.
+constexpr int kExactThreads = 64;
 template <bool kBf16, int kMode, bool kRotate>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kExactThreads)
 quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
                       float p_negexp, uint32_t sign_mask) {
     const int64_t ngroups = rows * gpr;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kExactThreads;
+    for (int64_t g = (int64_t)blockIdx.x * kExactThreads + threadIdx.x; g < ngroups; g += stride) {
         const int64_t r = g / gpr;
         const int64_t cg = g - r * gpr;
         float v[16];
@@ -447,12 +450,13 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
                                dim3((unsigned)blocks), dim3(kRowThreads), 0, stream, xb, rows, gpr,
                                ld_x, codes, scales, pe, pn, sign_mask);
     } else {
-        // the exact kernel: one group per thread where the grid allows
-        int64_t blocks = (ngroups + kThreads - 1) / kThreads;
-        if (blocks > 65536) blocks = 65536;
+        // the exact kernel: one group per thread where the grid allows (up to
+        // 2^24 groups per pass, then a grid-stride loop)
+        int64_t blocks = (ngroups + kExactThreads - 1) / kExactThreads;
+        if (blocks > 262144) blocks = 262144;
         hipLaunchKernelGGL((quantize_exact_kernel<false, kMode, kRotate>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, x, rows, gpr, ld_x, codes, scales, pe, pn,
-                           sign_mask);
+                           dim3(kExactThreads), 0, stream, x, rows, gpr, ld_x, codes, scales, pe,
+                           pn, sign_mask);
     }
     return hipGetLastError();
 }
