@@ -7,13 +7,13 @@
 // 6 |q| s' / 7 (times 2^E, which is exact: every result is fp32-normal).
 //
 // One lane per group (8 code bytes + 1 scale byte in, 16 values out), one
-// workgroup per 256 groups.
+// wave (64 groups) per workgroup.
 // The decode is branch-free and identical for both formats:
 //  * each nibble becomes an E4M3 byte -- FP4 s.e1e0.m -> s.00e1e0.m00 (the
 //    value c * 2^-6), INT4 s.mmm -> s.0000.mmm (the subnormal |q| * 2^-9) --
 //    and the hardware fp8 conversion yields m = +-c 2^-6 or +-|q| 2^-9
 //    exactly, sign and zero included;
-//  * y = fma(m, H, m * L) with a per-scale-byte pair from an LDS table:
+//  * y = fma(m, H, m * L) with a pair computed from the scale byte:
 //    FP4: H = s' 2^(E+6), L = 0, so y = c s' 2^E exactly; INT4:
 //    H = H' 2^(E+9) and L = fl32((6 s' - 7 H') * fl32(1/7)) 2^(E+9), where
 //    H' is 6 s'/7 rounded toward zero: a two-term split of 6 s'/7 whose fma
@@ -29,7 +29,7 @@
 namespace if4 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -38,10 +38,10 @@ __device__ __forceinline__ float e4m3_value_or_nan(uint32_t code7) {
     return code7 >= 8u ? __uint_as_float((code7 + 960u) << 20) : (float)code7 * 0.001953125f;
 }
 
-// Per-scale-byte decode table: H, L, nibble shift (2 for FP4, 0 for INT4).
+// Per-scale-byte decode constants: H, L, nibble shift (2 for FP4, 0 for INT4).
 struct Entry {
     float h, l;
-    uint32_t sh, pad;
+    uint32_t sh;
 };
 
 __device__ __forceinline__ Entry make_entry(uint32_t b, float p_exp) {
@@ -63,7 +63,6 @@ __device__ __forceinline__ Entry make_entry(uint32_t b, float p_exp) {
         e.l = 0.0f;
         e.sh = 2;
     }
-    e.pad = 0;
     return e;
 }
 
@@ -87,8 +86,6 @@ template <bool kBf16, bool kContig>
 __global__ void __launch_bounds__(kThreads)
 dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t rows, int64_t gpr, void* __restrict__ y, int64_t ld_y, float p_exp) {
-    __shared__ Entry table[256];
-
     const int64_t ngroups = rows * gpr;
     auto store = [&](int64_t g, const float* out) {
         int64_t off;
@@ -118,22 +115,19 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
         }
     };
 
-    // One group per thread, one workgroup per 256 groups: the thread's loads
-    // go out first (past the end they re-read the last group, whose store is
-    // then skipped, so no load sits behind a branch) and the decode table is
-    // built while they are in flight, behind an LDS-only barrier.  (Grid-stride
-    // loops over fewer workgroups, with the next group prefetched, measured
-    // up to 33% slower on a 470 MB output: they keep far fewer loads in
-    // flight.)
+    // One group per thread, one wave per workgroup: the thread's loads go
+    // out first (past the end they re-read the last group, whose store is
+    // then skipped, so no load sits behind a branch) and the scale byte's
+    // decode constants are computed by the thread itself -- no LDS table, no
+    // barrier (a per-workgroup table of 256 entries cost the same VALU work
+    // plus a barrier, and 12% more time at 256 x 256).  (Grid-stride loops
+    // over fewer workgroups, with the next group prefetched, measured up to
+    // 33% slower on a 470 MB output: they keep far fewer loads in flight.)
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t g = gid < ngroups - 1 ? gid : ngroups - 1;
     const uint2 cw = *reinterpret_cast<const uint2*>(codes + g * 8);
     const uint32_t b = scales[g];
-    table[threadIdx.x] = make_entry(threadIdx.x, p_exp);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    const Entry e = table[b];
+    const Entry e = make_entry(b, p_exp);
     float out[16];
     decode_word(cw.x, e, out);
     decode_word(cw.y, e, out + 8);
