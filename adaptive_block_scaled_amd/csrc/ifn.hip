@@ -204,8 +204,8 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 //  * quotients: u = |x|/s, and for INT the quotient on the INT grid, are
 //    approximated with reciprocals of s' (v_rcp_f32 refined by one Newton
 //    step: within 2^-24 (1 + 2^-22) relative) and snapped in the same fma to
-//    a grid that holds every midpoint exactly: u onto 2^-18 (+48, sums in
-//    [48, 64)); IF6's INT quotient 62|x|/(15 s) <= 34 onto 2^-17 (+64), as
+//    a grid that holds every midpoint exactly: IF6's u onto 2^-18 (+48, sums
+//    in [48, 64)); IF6's INT quotient 62|x|/(15 s) <= 34 onto 2^-17 (+64), as
 //    (|x| 62/64) * (64/(15 s)), the first product exact for bf16 and never
 //    overflowing; IF3's 3|x|/(4 s) onto 2^-19 (+16), as |x| * fl(0.75 r)
 //    (one more rounding: within 2^-23 (1 + 2^-22) relative).  The
@@ -220,15 +220,22 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 //    interleaves its two 16-value operands: slot 2j takes the first
 //    operand's value j, slot 2j + 1 the second's), and the matching decode
 //    (v_cvt_scalef32_pk32_f32_fp6) returns the grid values for the errors.
-//  * IF3 float codes: the snapped quotient against the three midpoints 0.5,
-//    1.5 and 3 of {0, 1, 2, 4} (> for 0.5 and 3, >= for 1.5: ties to even),
-//    each as one fma of the snapped sum (48 not subtracted) clamped to [0, 1].
+//  * IF3 float codes: the quotient against the three midpoints 0.5, 1.5 and 3
+//    of {0, 1, 2, 4} (> for 0.5 and 3, >= for 1.5: ties to even), each moved
+//    by less than the 2^-15 that separates a non-tie from it, toward the side
+//    its tie belongs to: 0.5 by one clamped fma, 1.5 and 3 as the binades of
+//    one affine function of u, whose exponent is the index.
+//  * IF3 packing: the chosen magnitudes shifted into the 48-bit field (the
+//    INT ones as whole magic-number floats, their constant part subtracted
+//    once), the signs gathered from the bf16 words by v_perm's sign-fill
+//    selectors.
 //  * INT magnitudes: adding 1.5 * 2^23 minus the snap offset rounds the
 //    snapped quotient to an integer (ties to even) in the float's low bits;
 //    an integer min clamps it to qmax.
 //  * errors: exactly the products and fmas of the reference (c dd s and
 //    |q| dn s are exact), in index order; IF3 subtracts them from dd |x|
-//    computed once (exact for bf16), which rounds the same difference once.
+//    computed once (exact for bf16), which rounds the same difference once
+//    (its float product as 2c times dd s / 2, the same exact value).
 //  * non-finite: an infinity makes the absmax infinite, a NaN the float
 //    error sum NaN; zero scales get zero reciprocals so the sums stay finite.
 __device__ __forceinline__ float refined_rcp(float d) {
@@ -254,9 +261,21 @@ __device__ __forceinline__ int scale_code_of(float a, float p_negexp) {
 // an IF6 group's code field
 constexpr uint32_t kIf6Sign[3] = {0x20820820u, 0x08208208u, 0x82082082u};
 
+// what the 1.5 * 2^23 of each INT3 element's rb adds to its code word when
+// rb is shifted into place whole (mod 2^32; elements 0-10 in word 0, 11-15 in
+// word 1)
+constexpr uint32_t if3_int_bias(int w) {
+    uint32_t k = 0;
+    for (int i = 0; i < 16; i++)
+        if ((i <= 10 ? 0 : 1) == w) k += 0x4B400000u << (3 * i - 32 * w);
+    return k;
+}
+constexpr uint32_t kIf3IntBias[2] = {if3_int_bias(0), if3_int_bias(1)};
+
 template <int kBits, int kMode>
-__device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_exp, float p_negexp,
-                                                uint32_t (&out)[3], uint32_t& byte) {
+__device__ __forceinline__ void fast_group_bf16(const float (&v)[16], const uint32_t (&xw)[8],
+                                                float p_exp, float p_negexp, uint32_t (&out)[3],
+                                                uint32_t& byte) {
     using F = Fmt<kBits>;
     float a = 0.0f;
 #pragma unroll
@@ -268,36 +287,36 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_ex
     float r = refined_rcp(sp);
     r = sc != 0 ? r : 0.0f;  // (rcp(0) is infinite)
     const float rs = r * p_negexp;                // ~ 1/s
+    const float rsk = rs * 0x1p18f;               // ~ 2^18 / s
+    const float ra = rs * 1.33331811f;            // ~ (4/3 - 2^-16) / s
     const float rs34 = (0.75f * r) * p_negexp;    // ~ 3/(4s), one more rounding
+    const float sdh = 0.5f * sdd;                 // exact
     float ef = 0.0f, ei = 0.0f;
-    uint32_t mq[3] = {0, 0, 0};
-    auto put = [](uint32_t(&f)[3], uint32_t c, int bit) {
-        f[bit >> 5] |= c << (bit & 31);
-        if ((bit & 31) + kBits > 32) f[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-    };
     static_assert(kBits == 3, "IF6 takes two groups at a time: if6_pair_bf16");
     {
-        uint32_t fiv[16], qv[16], sv[16];
+        uint32_t fiv[16], rbv[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const float ax = __builtin_fabsf(v[i]);
             // 3|x|, exact for bf16 (where it overflows, so does the reference's
             // fused 3|x| - c s dd, whose subtrahend is far below an ulp there)
             const float x3 = ax * F::kDd;
-            // u + 48, u = |x|/s snapped to a multiple of 2^-18 (sums in [48, 64));
-            // each step (u > 0.5, u >= 1.5, u > 3) is an fma of the snapped sum
-            // scaled by 2^18 -- an exact integer -- clamped to [0, 1]
-            const float u48 = __builtin_fmaf(ax, rs, 48.0f);
-            const float s1 = __builtin_amdgcn_fmed3f(
-                __builtin_fmaf(u48, 0x1p18f, -48.5f * 0x1p18f), 0.0f, 1.0f);
-            const float s2 = __builtin_amdgcn_fmed3f(
-                __builtin_fmaf(u48, 0x1p18f, 1.0f - 49.5f * 0x1p18f), 0.0f, 1.0f);
-            const float s3 = __builtin_amdgcn_fmed3f(
-                __builtin_fmaf(u48, 0x1p18f, -51.0f * 0x1p18f), 0.0f, 1.0f);
-            const float s12 = s1 + s2;
-            const int fi = (int)(s12 + s3);
-            const float cv = __builtin_fmaf(2.0f, s3, s12);  // 0, 1, 2, 4
-            const float df = __builtin_fmaf(-cv, sdd, x3);
+            // float index: u = |x|/s against the midpoints 0.5, 1.5 and 3 (ties
+            // to 0, 2 and 2).  An exact tie is the only quotient closer than
+            // 2^-15 to a midpoint, so each test may move its midpoint by less:
+            //  u > 0.5:  h = 2^18 (u - 0.5 - 2^-17) clamped to [0, 1] is 0 or 1
+            //            (the unclamped value is <= -1 or >= 1);
+            //  u >= 1.5 and u > 3: f = (4/3 - 2^-16) u + 2^-15 has f(1.5) =
+            //            2 + 2^-17 and f(3) = 4 - 2^-16; f raised to h and
+            //            capped below 8 (an infinite product included) has the
+            //            index as its exponent (frexp: [1, 2) -> 1, [2, 4) -> 2,
+            //            [4, 8) -> 3; below 1 -> 0 or less, raised to 0).
+            // The reciprocal's error moves f by under 2^-20 near the midpoints.
+            const float h = __builtin_amdgcn_fmed3f(__builtin_fmaf(ax, rsk, -131074.0f), 0.0f, 1.0f);
+            const float f = __builtin_amdgcn_fmed3f(__builtin_fmaf(ax, ra, 0x1p-15f), h, 7.99f);
+            const int fi = __builtin_elementwise_max(__builtin_amdgcn_frexp_expf(f), 0);
+            const float cv2 = __builtin_ldexpf(h, fi);  // twice the grid value: 0, 2, 4, 8
+            const float df = __builtin_fmaf(-cv2, sdh, x3);
             ef = __builtin_fmaf(df, df, ef);
             // 3|x|/(4s) snapped to a multiple of 2^-19 (sums in [16, 32)); 1.5 *
             // 2^23 - 16 more rounds it to an integer (ties even) in the low bits
@@ -308,15 +327,39 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], float p_ex
             const float di = __builtin_fmaf(-q, sdn, x3);
             ei = __builtin_fmaf(di, di, ei);
             fiv[i] = (uint32_t)fi;
-            qv[i] = rb & 3u;
-            sv[i] = __float_as_uint(v[i]) >> 31;
+            rbv[i] = rb;
         }
         const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
-        // the chosen format's codes, packed once
+        // the chosen magnitudes into the 48-bit field (element i at bits 3i,
+        // 3i + 1; element 10 ends word 0).  An INT magnitude goes in as the
+        // whole rb = 1.5 * 2^23 + |q|; what the constant adds is taken out after.
+        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int i = 0; i < 16; i++) put(mq, (use_int ? qv[i] : fiv[i]) | (sv[i] << 2), 3 * i);
-#pragma unroll
-        for (int w = 0; w < 3; w++) out[w] = mq[w];
+        for (int i = 0; i < 16; i++) {
+            const uint32_t c = use_int ? rbv[i] : fiv[i];
+            if (i <= 10) w0 += c << (3 * i);
+            else w1 += c << (3 * i - 32);
+        }
+        w0 -= use_int ? kIf3IntBias[0] : 0u;
+        w1 -= use_int ? kIf3IntBias[1] : 0u;
+        // sign bits (bit 3i + 2) from the bf16 words, whose bits 15 and 31 are
+        // elements 2j and 2j + 1: v_perm's selectors 8-11 fill a byte with
+        // bit 15 / 31 of its second source or bit 15 / 31 of its first, and 12
+        // gives a zero byte; each perm places at most one element per byte.
+        auto sgn = [](uint32_t hi, uint32_t lo, uint32_t sel, uint32_t mask) {
+            return __builtin_amdgcn_perm(hi, lo, sel) & mask;
+        };
+        w0 |= sgn(xw[2], xw[0], 0x0C0B0A08u, 0x00024004u)    // el 0 (b0), 4 (b1), 5 (b2)
+            | sgn(xw[3], xw[0], 0x0C0A0C09u, 0x00100020u)    // el 1 (b0), 6 (b2)
+            | sgn(xw[4], xw[1], 0x0A0C080Cu, 0x04000100u)    // el 2 (b1), 8 (b3)
+            | sgn(xw[4], xw[1], 0x0B0C090Cu, 0x20000800u)    // el 3 (b1), 9 (b3)
+            | sgn(xw[3], xw[3], 0x0C090C0Cu, 0x00800000u);   // el 7 (b2)
+        w1 |= sgn(xw[6], xw[5], 0x0C0C0B08u, 0x00000201u)    // el 10 (b0), 13 (b1)
+            | sgn(xw[7], xw[6], 0x0C0C0A08u, 0x00001040u)    // el 12 (b0), 14 (b1)
+            | sgn(xw[7], xw[5], 0x0C0C0B09u, 0x00008008u);   // el 11 (b0), 15 (b1)
+        out[0] = w0;
+        out[1] = w1;
+        out[2] = 0;
         byte = (uint32_t)sc | (use_int ? 0x80u : 0u);
     }
     if (sc == 0) {
@@ -472,10 +515,12 @@ quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64
         off = r * ld_x + (g - r * gpr) * 16;
     }
     float v[16];
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if constexpr (kBf16) {
         const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
         const uint4 a = p[0], b = p[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             v[2 * i] = __uint_as_float(w[i] << 16);
@@ -494,7 +539,7 @@ quantize_ifn_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int64
     }
     uint32_t out[3], byte;
     if constexpr (kBf16 && kBits == 3)
-        fast_group_bf16<kBits, kMode>(v, p_exp, p_negexp, out, byte);
+        fast_group_bf16<kBits, kMode>(v, w, p_exp, p_negexp, out, byte);
     else
         quantize_group<kBits, kMode>(v, p_exp, p_negexp, out, byte);
     if (gid >= ngroups) return;
