@@ -372,17 +372,28 @@ __device__ __forceinline__ void fast_group(const float (&v)[16],
 constexpr int kRowThreads = 64;
 constexpr int kGPT = 1;
 
+// The rotation's signs as xor words on the bf16 input words (element 2j in
+// the low half of word j, element 2j + 1 in the high half), computed on the
+// host so that each reaches the kernel as one scalar: a word split into its
+// two sign bits makes the compiler fuse the xor into a three-operand
+// instruction with two scalar operands, one of which then has to be copied
+// to a vector register for every group.
+struct SignWords {
+    uint32_t w[8];
+};
+
+inline SignWords sign_words(uint32_t sign_mask) {
+    SignWords f;
+    for (int j = 0; j < 8; j++)
+        f.w[j] = (((sign_mask >> (2 * j)) & 1u) << 15) | (((sign_mask >> (2 * j + 1)) & 1u) << 31);
+    return f;
+}
+
 template <int kMode, bool kContig, bool kRotate>
 __global__ void __launch_bounds__(kRowThreads)
 quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, int64_t ld_x,
                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float p_exp,
-                     float p_negexp, uint32_t sign_mask) {
-    // sign-bit xor words for the rotation: bf16 element 2j sits in the low
-    // half of input word j, element 2j + 1 in the high half
-    uint32_t flip[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-        flip[j] = (((sign_mask >> (2 * j)) & 1u) << 15) | (((sign_mask >> (2 * j + 1)) & 1u) << 31);
+                     float p_negexp, SignWords flip) {
     const int64_t ngroups = rows * gpr, last = ngroups - 1;
     const int64_t g0 = (int64_t)blockIdx.x * (kRowThreads * kGPT) + threadIdx.x;
     uint4 a[kGPT], b[kGPT];
@@ -407,7 +418,7 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
         uint32_t w[8] = {a[k].x, a[k].y, a[k].z, a[k].w, b[k].x, b[k].y, b[k].z, b[k].w};
         if constexpr (kRotate) {
 #pragma unroll
-            for (int i = 0; i < 8; i++) w[i] ^= flip[i];
+            for (int i = 0; i < 8; i++) w[i] ^= flip.w[i];
         }
         float v[16];
 #pragma unroll
@@ -416,11 +427,19 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
             v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
         if constexpr (kRotate) {
-            // rotate in fp32, then round back to bf16 (nearest even): the
-            // values the fast path needs are bf16-exact
+            // rotate in fp32, then round back to bf16 (nearest even), two
+            // values per conversion: the values the fast path needs are
+            // bf16-exact
             hadamard16(v);
 #pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = (float)(__bf16)v[i];
+            for (int i = 0; i < 8; i++) {
+                typedef float float2v __attribute__((ext_vector_type(2)));
+                typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+                const float2v f = {v[2 * i], v[2 * i + 1]};
+                const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+                v[2 * i] = __uint_as_float(u << 16);
+                v[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
+            }
         }
         uint32_t lo, hi, byte;
         fast_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
@@ -444,11 +463,11 @@ hipError_t launch(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8
         if (ld_x == cols)
             hipLaunchKernelGGL((quantize_bf16_kernel<kMode, true, kRotate>),
                                dim3((unsigned)blocks), dim3(kRowThreads), 0, stream, xb, rows, gpr,
-                               ld_x, codes, scales, pe, pn, sign_mask);
+                               ld_x, codes, scales, pe, pn, sign_words(sign_mask));
         else
             hipLaunchKernelGGL((quantize_bf16_kernel<kMode, false, kRotate>),
                                dim3((unsigned)blocks), dim3(kRowThreads), 0, stream, xb, rows, gpr,
-                               ld_x, codes, scales, pe, pn, sign_mask);
+                               ld_x, codes, scales, pe, pn, sign_words(sign_mask));
     } else {
         // the exact kernel: one group per thread where the grid allows (up to
         // 2^24 groups per pass, then a grid-stride loop)
