@@ -206,8 +206,8 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 //    step: within 2^-24 (1 + 2^-22) relative) and snapped in the same fma to
 //    a grid that holds every midpoint exactly: IF6's u onto 2^-18 (+48, sums
 //    in [48, 64)); IF6's INT quotient 62|x|/(15 s) <= 34 onto 2^-17 (+64), as
-//    (|x| 62/64) * (64/(15 s)), the first product exact for bf16 and never
-//    overflowing; IF3's 3|x|/(4 s) onto 2^-19 (+16), as |x| * fl(0.75 r)
+//    62|x| (exact for bf16, and shared with both error terms) times the
+//    reciprocal of 15 s; IF3's 3|x|/(4 s) onto 2^-19 (+16), as |x| * fl(0.75 r)
 //    (one more rounding: within 2^-23 (1 + 2^-22) relative).  The
 //    approximation error at the largest midpoint that matters (7.25, 30.5,
 //    2.5) stays below half the snap grid, so a value on a midpoint snaps onto
@@ -233,9 +233,9 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], float p_exp
 //    snapped quotient to an integer (ties to even) in the float's low bits;
 //    an integer min clamps it to qmax.
 //  * errors: exactly the products and fmas of the reference (c dd s and
-//    |q| dn s are exact), in index order; IF3 subtracts them from dd |x|
-//    computed once (exact for bf16), which rounds the same difference once
-//    (its float product as 2c times dd s / 2, the same exact value).
+//    |q| dn s are exact), in index order; both formats subtract them from
+//    dd |x| computed once (exact for bf16), which rounds the same difference
+//    once (IF3's float product as 2c times dd s / 2, the same exact value).
 //  * non-finite: an infinity makes the absmax infinite, a NaN the float
 //    error sum NaN; zero scales get zero reciprocals so the sums stay finite.
 __device__ __forceinline__ float refined_rcp(float d) {
@@ -386,6 +386,7 @@ __device__ __forceinline__ void if6_pair_bf16(const float (&v)[2][16], float p_e
     typedef float v32f __attribute__((ext_vector_type(32)));
     typedef uint32_t v6u __attribute__((ext_vector_type(6)));
     v16f ev, od;  // signed snapped quotients of the even / odd elements
+    float x62[2][16];  // 62 |x|
     float a[2], ei[2] = {0.0f, 0.0f}, sdd[2];
     int sc[2];
     uint32_t mq[2][3] = {{0, 0, 0}, {0, 0, 0}};
@@ -403,21 +404,28 @@ __device__ __forceinline__ void if6_pair_bf16(const float (&v)[2][16], float p_e
         r = sc[h] != 0 ? r : 0.0f;  // (rcp(0) is infinite)
         rq = sc[h] != 0 ? rq : 0.0f;
         const float rs = r * p_negexp;          // ~ 1/s
-        rq *= 64.0f * p_negexp;                 // ~ 64 / (15 s)
+        rq *= p_negexp;                         // ~ 1 / (15 s)
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const float ax = __builtin_fabsf(v[h][i]);
+            // 62 |x|: exact for bf16 (5 + 8 significant bits).  Where it
+            // overflows, the reference's fused 62|x| - c 62 s and 62|x| - |q| 15 s
+            // overflow too: s <= 448 * 2^64 puts both subtrahends far below an
+            // ulp there, and 62|x|, a multiple of 2^116 there, is never the
+            // rounding midpoint to infinity.
+            x62[h][i] = ax * F::kDd;
             const float u = __builtin_copysignf(__builtin_fmaf(ax, rs, 48.0f) - 48.0f, v[h][i]);
             if (i & 1)
                 od[8 * h + (i >> 1)] = u;
             else
                 ev[8 * h + (i >> 1)] = u;
-            // INT: 1.5 * 2^23 + |q| in the float's bits, |q| clamped to 31
-            const float t = __builtin_fmaf(ax * 0.96875f, rq, 64.0f);
+            // INT: 1.5 * 2^23 + |q| in the float's bits, |q| clamped to 31;
+            // 62|x| / (15 s) from the exact 62|x| and the reciprocal
+            const float t = __builtin_fmaf(x62[h][i], rq, 64.0f);
             const uint32_t rb =
                 __builtin_elementwise_min(__float_as_uint(t + 12582848.0f), 0x4B40001Fu);
             const float q = __uint_as_float(rb) - 12582912.0f;
-            const float di = __builtin_fmaf(ax, F::kDd, -(q * sdn));
+            const float di = __builtin_fmaf(-q, sdn, x62[h][i]);  // |q| 15 s exact
             ei[h] = __builtin_fmaf(di, di, ei[h]);
             const int bit = 6 * i;
             const uint32_t m = rb & 31u;
@@ -433,8 +441,7 @@ __device__ __forceinline__ void if6_pair_bf16(const float (&v)[2][16], float p_e
         float ef = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            const float df = __builtin_fmaf(__builtin_fabsf(v[h][i]), F::kDd,
-                                            -(__builtin_fabsf(c[16 * h + i]) * sdd[h]));
+            const float df = __builtin_fmaf(-__builtin_fabsf(c[16 * h + i]), sdd[h], x62[h][i]);
             ef = __builtin_fmaf(df, df, ef);
         }
         const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei[h] < ef));
