@@ -372,6 +372,21 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], const uint
     }
 }
 
+// what the 1.5 * 2^23 of each INT6 element's rb adds to the three code words
+// when rb is shifted into its field whole (mod 2^32; a straddling field's
+// upper part goes to the next word, where 1.5 * 2^23 >> (32 - bit) is exact:
+// its low 22 bits are zero)
+constexpr uint32_t if6_int_bias(int w) {
+    uint32_t k = 0;
+    for (int i = 0; i < 16; i++) {
+        const int bit = 6 * i;
+        if ((bit >> 5) == w) k += 0x4B400000u << (bit & 31);
+        if ((bit & 31) + 6 > 32 && (bit >> 5) + 1 == w) k += 0x4B400000u >> (32 - (bit & 31));
+    }
+    return k;
+}
+constexpr uint32_t kIf6IntBias[3] = {if6_int_bias(0), if6_int_bias(1), if6_int_bias(2)};
+
 // IF6, two groups at a time: the E2M3 conversion takes 32 values, slot 2j
 // from its first operand's value j and slot 2j + 1 from the second's, so the
 // even elements of groups 0 and 1 go to the first operand (positions 0-7 and
@@ -427,12 +442,18 @@ __device__ __forceinline__ void if6_pair_bf16(const float (&v)[2][16], float p_e
             const float q = __uint_as_float(rb) - 12582912.0f;
             const float di = __builtin_fmaf(-q, sdn, x62[h][i]);  // |q| 15 s exact
             ei[h] = __builtin_fmaf(di, di, ei[h]);
+            // rb = 1.5 * 2^23 + |q| shifted into the 6-bit field whole (its
+            // constant part taken out once per word below); a field that
+            // straddles two words puts its upper bits into the next one
             const int bit = 6 * i;
-            const uint32_t m = rb & 31u;
-            mq[h][bit >> 5] |= m << (bit & 31);
-            if ((bit & 31) + 6 > 32) mq[h][(bit >> 5) + 1] |= m >> (32 - (bit & 31));
+            mq[h][bit >> 5] += rb << (bit & 31);
+            if ((bit & 31) + 6 > 32) mq[h][(bit >> 5) + 1] += rb >> (32 - (bit & 31));
         }
     }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int w = 0; w < 3; w++) mq[h][w] -= kIf6IntBias[w];
     const auto fcv = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
     const v6u fc = __builtin_bit_cast(v6u, fcv);
     const v32f c = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(fcv, 1.0f);

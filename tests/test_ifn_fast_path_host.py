@@ -1,5 +1,6 @@
-"""Host checks of two constructions in the IF3 bf16 fast path
-(adaptive_block_scaled_amd/csrc/ifn.hip, fast_group_bf16), run on the CPU.
+"""Host checks of constructions in the IF3 and IF6 bf16 fast paths
+(adaptive_block_scaled_amd/csrc/ifn.hip: fast_group_bf16, if6_pair_bf16), run
+on the CPU.
 
 * The float index: the kernel moves each midpoint of the FP3 E2M0 grid
   {0, 1, 2, 4} by less than the distance of the nearest non-tie quotient, and
@@ -12,6 +13,7 @@
 * The packing: the magnitudes go into the 48-bit field with the INT ones as
   whole magic-number floats (the constant part subtracted once per word), and
   the sign bits come from the bf16 words through v_perm sign-fill selectors.
+  IF6 packs its INT magnitudes the same way into 96-bit fields.
   The constants are read from the kernel source and checked against the field
   layout (element i at bits 3i .. 3i+2, sign at 3i + 2) on random words.
 
@@ -123,3 +125,31 @@ def test_if3_int_bias():
         field = sum(q[i] << (3 * i) for i in range(16))
         assert (acc[0] - bias[0]) & 0xFFFFFFFF == field & 0xFFFFFFFF
         assert (acc[1] - bias[1]) & 0xFFFFFFFF == field >> 32
+
+
+def test_if6_int_bias():
+    # IF6's INT magnitudes: 1.5 * 2^23 + |q| (|q| <= 31) shifted into 6-bit fields
+    # whole, a straddling field's upper bits into the next word; the constant
+    # part, restated from the layout, must come out exactly
+    src = open(SRC).read()
+    assert "0x4B400000u >> (32 - (bit & 31))" in src and "mq[h][bit >> 5] += rb << (bit & 31);" in src
+    bias = [0, 0, 0]
+    for i in range(16):
+        bit = 6 * i
+        bias[bit >> 5] = (bias[bit >> 5] + ((0x4B400000 << (bit & 31)) & 0xFFFFFFFF)) & 0xFFFFFFFF
+        if (bit & 31) + 6 > 32:
+            w = (bit >> 5) + 1
+            bias[w] = (bias[w] + (0x4B400000 >> (32 - (bit & 31)))) & 0xFFFFFFFF
+    rng = random.Random(7)
+    for _ in range(5000):
+        q = [rng.randrange(32) for _ in range(16)]
+        acc = [0, 0, 0]
+        for i in range(16):
+            rb, bit = 0x4B400000 + q[i], 6 * i
+            acc[bit >> 5] = (acc[bit >> 5] + ((rb << (bit & 31)) & 0xFFFFFFFF)) & 0xFFFFFFFF
+            if (bit & 31) + 6 > 32:
+                acc[(bit >> 5) + 1] = (acc[(bit >> 5) + 1] + (rb >> (32 - (bit & 31)))) & 0xFFFFFFFF
+        field = sum(q[i] << (6 * i) for i in range(16))
+        for w in range(3):
+            assert (acc[w] - bias[w]) & 0xFFFFFFFF == (field >> (32 * w)) & 0xFFFFFFFF
+
