@@ -17,8 +17,8 @@
 // little-endian 2*bits-byte code field.
 //
 // One group per thread (IF6 from bf16: two), one-wave workgroups for the
-// quantizes and 256-thread ones for the dequantize, the thread's loads issued
-// first.  Every rounding is decided exactly (exact comparisons, or the
+// quantizes and the IF3 dequantize and 256-thread ones for the IF6
+// dequantize, the thread's loads issued first.  Every rounding is decided exactly (exact comparisons, or the
 // exact sign of one fma), ties to the even index -- valid for any fp32 input
 // -- in branch-free code.
 #include <hip/hip_runtime.h>
@@ -29,7 +29,7 @@
 namespace if4 {
 namespace {
 
-constexpr int kThreads = 256;  // dequantize: one workgroup builds its LDS tables for 256 groups
+constexpr int kThreads = 256;  // IF6 dequantize: one workgroup builds its LDS tables for 256 groups
 constexpr int kQThreads = 64;  // quantizes (no LDS): one-wave workgroups fill the chip sooner
 
 template <int kBits>
@@ -695,6 +695,90 @@ dequantize_ifn_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
     }
 }
 
+// IF3 dequantize in registers: each lane computes its scale byte's decode
+// pair, turns its 16 three-bit codes into E4M3 bytes by one byte permute per
+// four codes from an 8-byte table (FP3: s.0.0mm.000 = grid value 2^-6; INT3:
+// s.0000.0mm = |q| 2^-9, the table picked by the flag), converts them with
+// the hardware fp8 conversion and scales them by fma(m, H, m L) -- the same
+// products as the table path, so the same results.  One wave per workgroup,
+// and the workgroup order paired on the XCDs as in the IF4 dequantize (two
+// neighbouring waves share a 128-byte line of scale bytes).
+constexpr int kD3Threads = 64;
+template <bool kBf16, bool kContig>
+__global__ void __launch_bounds__(kD3Threads)
+dequantize_if3_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                      int64_t rows, int64_t gpr, void* __restrict__ y, int64_t ld_y, float p_exp) {
+    using F = Fmt<3>;
+    const int64_t ngroups = rows * gpr;
+    const unsigned full = gridDim.x & ~15u, bj = blockIdx.x & 15u;
+    const int64_t blk = blockIdx.x < full ? (int64_t)(blockIdx.x - bj + 2u * (bj & 7u) + (bj >> 3))
+                                          : (int64_t)blockIdx.x;
+    const int64_t gid = blk * kD3Threads + threadIdx.x;
+    const int64_t g = gid < ngroups - 1 ? gid : ngroups - 1;
+    const uint16_t* c = reinterpret_cast<const uint16_t*>(codes + g * 6);
+    const uint32_t w0 = (uint32_t)c[0] | ((uint32_t)c[1] << 16), w1 = c[2];
+    const uint32_t b = scales[g];
+
+    const float sp = (b & 0x7Fu) == 0x7Fu ? __uint_as_float(0x7FC00000u) : e4m3_value(b & 0x7Fu);
+    const bool isint = (b & 0x80u) != 0;
+    float hh, ll;
+    {
+        const float num = F::kDn * sp;  // exact
+        float h = num / F::kDd;
+        if (__builtin_fmaf(-h, F::kDd, num) < 0.0f) h = __uint_as_float(__float_as_uint(h) - 1u);
+        const float l = __builtin_fmaf(-h, F::kDd, num) * (1.0f / F::kDd);
+        hh = isint ? h * (p_exp * 512.0f) : sp * (p_exp * 64.0f);
+        ll = isint ? l * (p_exp * 512.0f) : 0.0f;
+    }
+    const uint32_t tlo = isint ? 0x03020100u : 0x18100800u;
+    const uint32_t thi = isint ? 0x83828180u : 0x98908880u;
+    auto spread = [](uint32_t t) {  // four 3-bit codes into the low bits of four bytes
+        return (t & 7u) | ((t << 5) & 0x700u) | ((t << 10) & 0x70000u) | ((t << 15) & 0x7000000u);
+    };
+    const uint32_t e[4] = {
+        __builtin_amdgcn_perm(thi, tlo, spread(w0)),
+        __builtin_amdgcn_perm(thi, tlo, spread(w0 >> 12)),
+        __builtin_amdgcn_perm(thi, tlo, spread((w0 >> 24) | (w1 << 8))),
+        __builtin_amdgcn_perm(thi, tlo, spread(w1 >> 4)),
+    };
+    float out[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e[k], 1.0f, false);
+        const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e[k], 1.0f, true);
+        const float m[4] = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int j = 0; j < 4; j++) out[4 * k + j] = __builtin_fmaf(m[j], hh, m[j] * ll);
+    }
+    if (gid >= ngroups) return;
+    int64_t off;
+    if constexpr (kContig) {
+        off = gid * 16;
+    } else {
+        const int64_t r = gid / gpr;
+        off = r * ld_y + (gid - r * gpr) * 16;
+    }
+    if constexpr (kBf16) {
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            bf16x2 t;
+            t[0] = (__bf16)out[2 * i];
+            t[1] = (__bf16)out[2 * i + 1];
+            o[i] = __builtin_bit_cast(uint32_t, t);
+        }
+        uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + off);
+        p[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        p[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + off);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            p[i] = make_float4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    }
+}
+
 template <int kBits, int kMode, bool kBf16>
 hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                     uint8_t* scales, int32_t scale_exp, hipStream_t stream) {
@@ -746,21 +830,38 @@ template <int kBits>
 hipError_t dispatch_dq(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                        int32_t scale_exp, void* y, int bf16, int64_t ld_y, hipStream_t stream) {
     const int64_t gpr = cols / 16;
-    const int64_t blocks = (rows * gpr + kThreads - 1) / kThreads;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-#define IF4_DQN(B, C)                                                                  \
-    hipLaunchKernelGGL((dequantize_ifn_kernel<kBits, B, C>), dim3((unsigned)blocks),            \
-                       dim3(kThreads), 0, stream, codes, scales, rows, gpr, y, ld_y,            \
-                       pow2f(scale_exp))
     const bool contig = ld_y == cols;
-    if (bf16) {
-        if (contig) IF4_DQN(true, true);
-        else IF4_DQN(true, false);
-    } else {
-        if (contig) IF4_DQN(false, true);
-        else IF4_DQN(false, false);
-    }
+    if constexpr (kBits == 3) {  // registers only
+        const int64_t blocks = (rows * gpr + kD3Threads - 1) / kD3Threads;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define IF4_DQ3(B, C)                                                                          \
+        hipLaunchKernelGGL((dequantize_if3_kernel<B, C>), dim3((unsigned)blocks),              \
+                           dim3(kD3Threads), 0, stream, codes, scales, rows, gpr, y, ld_y,     \
+                           pow2f(scale_exp))
+        if (bf16) {
+            if (contig) IF4_DQ3(true, true);
+            else IF4_DQ3(true, false);
+        } else {
+            if (contig) IF4_DQ3(false, true);
+            else IF4_DQ3(false, false);
+        }
+#undef IF4_DQ3
+    } else {  // per-workgroup LDS tables
+        const int64_t blocks = (rows * gpr + kThreads - 1) / kThreads;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define IF4_DQN(B, C)                                                                          \
+        hipLaunchKernelGGL((dequantize_ifn_kernel<kBits, B, C>), dim3((unsigned)blocks),       \
+                           dim3(kThreads), 0, stream, codes, scales, rows, gpr, y, ld_y,       \
+                           pow2f(scale_exp))
+        if (bf16) {
+            if (contig) IF4_DQN(true, true);
+            else IF4_DQN(true, false);
+        } else {
+            if (contig) IF4_DQN(false, true);
+            else IF4_DQN(false, false);
+        }
 #undef IF4_DQN
+    }
     return hipGetLastError();
 }
 
