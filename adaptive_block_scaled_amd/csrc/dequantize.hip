@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "if4_internal.h"
+#include "xcd_order.h"
 
 namespace if4 {
 namespace {
@@ -80,18 +81,6 @@ __device__ __forceinline__ void decode_word(uint32_t w, const Entry& e, float* o
     const float m[8] = {e01[0], o01[0], e01[1], o01[1], e23[0], o23[0], e23[1], o23[1]};
 #pragma unroll
     for (int i = 0; i < 8; i++) out[i] = __builtin_fmaf(m[i], e.h, m[i] * e.l);
-}
-
-// Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b mod 8),
-// and two neighbouring one-wave workgroups share a 128-byte line of scale
-// bytes (64 each): on two XCDs both L2s would fetch it (11% more HBM reads on
-// a large tensor).  Within each run of 16 workgroups this permutation gives
-// the groups of workgroups 2k and 2k + 1 to workgroups on the same XCD; the
-// last gridDim % 16 keep their own.  (Giving each XCD one contiguous eighth
-// of the tensor also fetches each line once, but streams 8% slower.)
-__device__ __forceinline__ int64_t xcd_paired_block(unsigned b, unsigned nb) {
-    const unsigned full = nb & ~15u, j = b & 15u;
-    return b < full ? (int64_t)(b - j + 2u * (j & 7u) + (j >> 3)) : (int64_t)b;
 }
 
 template <bool kBf16, bool kContig>

@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "if4_internal.h"
+#include "xcd_order.h"
 
 namespace if4 {
 namespace {
@@ -710,10 +711,7 @@ dequantize_if3_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
                       int64_t rows, int64_t gpr, void* __restrict__ y, int64_t ld_y, float p_exp) {
     using F = Fmt<3>;
     const int64_t ngroups = rows * gpr;
-    const unsigned full = gridDim.x & ~15u, bj = blockIdx.x & 15u;
-    const int64_t blk = blockIdx.x < full ? (int64_t)(blockIdx.x - bj + 2u * (bj & 7u) + (bj >> 3))
-                                          : (int64_t)blockIdx.x;
-    const int64_t gid = blk * kD3Threads + threadIdx.x;
+    const int64_t gid = xcd_paired_block(blockIdx.x, gridDim.x) * kD3Threads + threadIdx.x;
     const int64_t g = gid < ngroups - 1 ? gid : ngroups - 1;
     const uint16_t* c = reinterpret_cast<const uint16_t*>(codes + g * 6);
     const uint32_t w0 = (uint32_t)c[0] | ((uint32_t)c[1] << 16), w1 = c[2];
