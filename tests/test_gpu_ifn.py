@@ -100,6 +100,25 @@ def test_wide_values_and_exponents(oracle_mod, bits, dtype, e):
 
 
 @pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("tdt", ["f32", "bf16"])
+def test_dequantize_strided_output_ragged(oracle_mod, bits, tdt):
+    """Dequantize into rows of a wider buffer: 129 x 4112 is 33153 groups (519
+    one-wave workgroups for IF3: 32 full runs of 16 for the XCD pairing and a
+    remainder of 7), the padding past each row left untouched."""
+    x = draw((129, 4112), "normal", 21, "bf16")
+    c, s = check_q(oracle_mod, x, bits, "bf16", -3, label="dq strided")
+    want = oracle_mod.dequantize_ifn(c.cpu().numpy(), s.cpu().numpy(), bits, -3)
+    dt = torch.float32 if tdt == "f32" else torch.bfloat16
+    big = torch.full((129, 4112 + 16), 7.0, dtype=dt, device="cuda")
+    _if4().dequantize_ifn(c, s, bits, -3, out=big[:, :4112])
+    torch.cuda.synchronize()
+    got = big[:, :4112].float().cpu().numpy()
+    wantt = torch.from_numpy(want).to(dt).float().numpy()
+    assert np.array_equal(got.view(np.uint32), wantt.view(np.uint32))
+    assert bool((big[:, 4112:] == 7.0).all())
+
+
+@pytest.mark.parametrize("bits", [3, 6])
 def test_edge_groups_and_strided_input(oracle_mod, bits):
     g = np.zeros((10, 16), np.float32)
     g[1, :] = -0.0
