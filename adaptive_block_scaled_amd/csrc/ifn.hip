@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "if4_internal.h"
 #include "xcd_order.h"
 
@@ -296,6 +298,15 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], const uint
     static_assert(kBits == 3, "IF6 takes two groups at a time: if6_pair_bf16");
     {
         uint32_t fiv[16], rbv[16];
+        // The INT clamp |q| <= 3 can only act when s' is an E4M3 subnormal
+        // (codes 1-7) or the 448 code (where a'/4 may lie far above it).  For
+        // every other scale s' >= (a'/4) / (1 + 2^-4) -- rounding to three
+        // mantissa bits moves a value down by at most 2^-4 of its binade's
+        // base -- so 3|x|/(4s) <= 3 * 1.0625 = 3.1875 (plus the snapped
+        // quotient's error) rounds to at most 3 without it; the loop runs
+        // without the clamp when no lane of the wave needs it.
+        auto pass = [&](auto clamp_c) {
+        constexpr bool kClamp = decltype(clamp_c)::value;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const float ax = __builtin_fabsf(v[i]);
@@ -322,14 +333,20 @@ __device__ __forceinline__ void fast_group_bf16(const float (&v)[16], const uint
             // 3|x|/(4s) snapped to a multiple of 2^-19 (sums in [16, 32)); 1.5 *
             // 2^23 - 16 more rounds it to an integer (ties even) in the low bits
             const float t = __builtin_fmaf(ax, rs34, 16.0f);
-            const uint32_t rb =
-                __builtin_elementwise_min(__float_as_uint(t + 12582896.0f), 0x4B400003u);
+            uint32_t rb = __float_as_uint(t + 12582896.0f);
+            if constexpr (kClamp) rb = __builtin_elementwise_min(rb, 0x4B400003u);
             const float q = __uint_as_float(rb) - 12582912.0f;
             const float di = __builtin_fmaf(-q, sdn, x3);
             ei = __builtin_fmaf(di, di, ei);
             fiv[i] = (uint32_t)fi;
             rbv[i] = rb;
         }
+        };
+        const bool need_clamp = (uint32_t)(sc - 1) < 7u || sc >= 126;
+        if (__builtin_amdgcn_ballot_w64(need_clamp) != 0)
+            pass(std::true_type{});
+        else
+            pass(std::false_type{});
         const bool use_int = kMode == 2 ? true : (kMode == 1 ? false : (ei < ef));
         // the chosen magnitudes into the 48-bit field (element i at bits 3i,
         // 3i + 1; element 10 ends word 0).  An INT magnitude goes in as the

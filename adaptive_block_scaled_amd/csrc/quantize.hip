@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "if4_internal.h"
 
 namespace if4 {
@@ -248,7 +250,7 @@ quantize_exact_kernel(const void* __restrict__ x, int64_t rows, int64_t gpr, int
 
 // One group of bf16-exact values, fast path (see above): codes and flagged
 // scale byte, identical to exact_group for bf16 inputs.
-template <int kMode>
+template <int kMode, bool kElideClamp = false>
 __device__ __forceinline__ void fast_group(const float (&v)[16],
                                            float p_exp, float p_negexp, uint32_t& lo,
                                            uint32_t& hi, uint32_t& byte) {
@@ -309,24 +311,43 @@ __device__ __forceinline__ void fast_group(const float (&v)[16],
         c[12] = d6[0]; c[13] = d6[1]; c[14] = d7[0]; c[15] = d7[1];
     }
 
-    // INT4 magnitudes and both error sums, index order 0..15
+    // INT4 magnitudes and both error sums, index order 0..15.  The clamp
+    // |q| <= 7 can only act when s' is an E4M3 subnormal (codes 1-7, spaced
+    // 2^-9 apart, so s' may sit far below a'/6) or when a'/6 reaches 448 (the
+    // scale saturates).  For every other scale s' >= (a'/6) / (1 + 2^-4) --
+    // rounding to three mantissa bits moves a value down by at most 2^-4 of
+    // its binade's base -- so 7|x|/(6s) <= 7 * 1.0625 = 7.4375 (plus the
+    // snapped quotient's error, below 2^-20) rounds to at most 7 without it.
+    // With kElideClamp the clamp is taken out of the loop when no lane of the
+    // wave needs it, at the cost of a second copy of the loop: 16 fewer VALU
+    // per group on the row kernel (3-5% faster on 86-470 MB tensors); the x^T
+    // kernels gain nothing from it and the rotating kernel runs 1-2% slower.
     float ef = 0.0f, ei = 0.0f;
     uint32_t rq[16];
+    auto int4_pass = [&](auto clamp_c) {
+        constexpr bool kClamp = decltype(clamp_c)::value;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const float xa = __builtin_fabsf(v[i]);
-        const float X = 7.0f * v[i];
-        const float t = __builtin_fmaf(xa, k7, 48.0f);
-        // 1.5*2^23 + |q|, clamped to |q| <= 7 (positive floats order as their bits)
-        const float r = __uint_as_float(
-            __builtin_elementwise_min(__float_as_uint(t + 12582864.0f), 0x4B400007u));
-        rq[i] = __float_as_uint(r);
-        const float q = r - 12582912.0f;
-        const float df = __builtin_fmaf(-c[i], s7, X);
-        const float di = __builtin_fmaf(-q, s6, __builtin_fabsf(X));
-        ef = __builtin_fmaf(df, df, ef);
-        ei = __builtin_fmaf(di, di, ei);
-    }
+        for (int i = 0; i < 16; i++) {
+            const float xa = __builtin_fabsf(v[i]);
+            const float X = 7.0f * v[i];
+            const float t = __builtin_fmaf(xa, k7, 48.0f);
+            // 1.5*2^23 + |q|, clamped to |q| <= 7 (positive floats order as
+            // their bits)
+            uint32_t rb = __float_as_uint(t + 12582864.0f);
+            if constexpr (kClamp) rb = __builtin_elementwise_min(rb, 0x4B400007u);
+            rq[i] = rb;
+            const float q = __uint_as_float(rb) - 12582912.0f;
+            const float df = __builtin_fmaf(-c[i], s7, X);
+            const float di = __builtin_fmaf(-q, s6, __builtin_fabsf(X));
+            ef = __builtin_fmaf(df, df, ef);
+            ei = __builtin_fmaf(di, di, ei);
+        }
+    };
+    const bool need_clamp = (sc - 1u < 7u) || (q6 >= 448.0f);
+    if (!kElideClamp || __builtin_amdgcn_ballot_w64(need_clamp) != 0)
+        int4_pass(std::true_type{});
+    else
+        int4_pass(std::false_type{});
     // gather |q| (low byte of each float) into nibbles: even elements in
     // bits 0-2, odd elements in bits 4-6 of each byte
     uint32_t i0, i1;
@@ -442,7 +463,7 @@ quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t gpr, 
             }
         }
         uint32_t lo, hi, byte;
-        fast_group<kMode>(v, p_exp, p_negexp, lo, hi, byte);
+        fast_group<kMode, !kRotate>(v, p_exp, p_negexp, lo, hi, byte);
         if (g < ngroups) {
             *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(lo, hi);
             scales[g] = (uint8_t)byte;
