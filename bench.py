@@ -157,11 +157,11 @@ def main():
     # dequantize of W's codes to bf16, timed on its own after the step loop;
     # its 587 MB working set exceeds the 256 MB last-level cache, so repeated
     # launches stream from HBM (A's 168 MB would partly stay cached)
-    # (8 warm-up launches: the clock settles over the first few launches of a
-    # kernel that follows a different one)
+    # (each kernel first runs back to back for WARM_S seconds: the clock
+    # settles over the first tens of milliseconds of a kernel that follows
+    # idle time or different work)
     def time_launches(fn, n=20):
-        for _ in range(8):
-            fn()
+        warm_for(torch, [fn])
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record()
         for _ in range(n):
@@ -315,14 +315,34 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def mean_launch_ms(torch, calls, n=100, warmup=200, batches=3):
+# Warm-up before each kernel is timed on its own: back-to-back launches for
+# this long.  After idle time or memory-bound work the clock needs tens of
+# milliseconds of VALU-heavy work to reach its sustained level (the 8192x4096
+# quantize measured 21.6 us per launch after 200 launches from idle, 17.2 us
+# after 1000 and 16.8 us after 5000 or 20000, while a device copy of the
+# same bytes stays at 17.7-17.9 us throughout).
+WARM_S = 0.1
+
+
+def warm_for(torch, calls, seconds=WARM_S):
+    """Launch `calls` in turn, back to back, until `seconds` have passed
+    (at least 200 launches)."""
+    t0, i = time.perf_counter(), 0
+    while True:
+        for _ in range(50):
+            calls[i % len(calls)]()
+            i += 1
+        torch.cuda.synchronize()
+        if i >= 200 and time.perf_counter() - t0 >= seconds:
+            return
+
+
+def mean_launch_ms(torch, calls, n=100, batches=3):
     """Time per launch: the median over `batches` of the mean of n
     back-to-back launches between one pair of HIP events, cycling through
     `calls` (one per buffer set, so that consecutive launches touch different
-    memory).  The long warm-up lets the clock settle after the heavier work
-    timed before."""
-    for i in range(warmup):
-        calls[i % len(calls)]()
+    memory), after WARM_S seconds of the same launches."""
+    warm_for(torch, calls)
     per = []
     for _ in range(batches):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
