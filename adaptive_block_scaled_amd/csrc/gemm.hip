@@ -159,6 +159,8 @@ __device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, GroupScal
 // Word 3 of a buffer resource for plain byte-addressed dword loads on gfx9
 // class chips (no format conversion, no swizzle).
 constexpr int kRawBufferFlags = 0x00020000;
+// cache-policy operand of a buffer store: non-temporal (the nt bit)
+constexpr int kNonTemporal = 2;
 
 struct Operand {
     __amdgpu_buffer_rsrc_t codes, scales;
@@ -611,6 +613,37 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // (the lane half recomputed from the lane id, so that nothing computed
     // before the K loop has to stay live across it)
     const int eh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
+    // Stores go through a buffer resource based at the tile's first output
+    // and sized to the tile's rows that exist (a store to a row past M falls
+    // outside it and is dropped by the hardware): the lane's column and row
+    // half are one vector offset, each row of the wave one scalar offset and
+    // each 32-column block an immediate, with one lane test per block for
+    // columns past N -- no 64-bit address arithmetic per store.  (Offsets
+    // are 32-bit; a row stride beyond 2^21 floats takes the general path.)
+    if ((uint64_t)ldc * (4 * BM) < (1ull << 31)) {
+        const uint32_t ld4 = (uint32_t)ldc * 4;
+        const int rows_valid = (int)(M - m0 < BM ? M - m0 : BM);
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(c + m0 * ldc + n0), 0, (int)((uint32_t)rows_valid * ld4), kRawBufferFlags);
+        const int cl = lane & 31;
+        const uint32_t vo = (uint32_t)cl * 4 + (uint32_t)(4 * eh) * ld4;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (n0 + 32 * j + cl < N) {
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int so = (64 * wv + 32 * i + 8 * (r >> 2) + (r & 3)) * (int)ld4;
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __float_as_uint(__builtin_amdgcn_ldexpf(acc[i][j][r], out_exp)), crs,
+                            vo + j * 128, so, kNonTemporal);
+                    }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll

@@ -58,6 +58,30 @@ def test_ragged_shapes(oracle_mod, mnk):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("mn_ld", [(261, 77, 80), (9, 300, (1 << 21) + 40)])
+def test_stores_stay_inside_c(oracle_mod, mn_ld):
+    """Partial tiles on the bottom and right edges, C a view into a larger
+    buffer: every output of C[:M, :N] is right, and the columns past N and
+    the three rows past M of the buffer keep their sentinel.  A row stride
+    above 2^21 floats takes the kernel's general store path."""
+    M, N, ldc = mn_ld
+    K = 256
+    print(f"[gemm] edges M={M} N={N} K={K} ldc={ldc}", flush=True)
+    from adaptive_block_scaled_amd import if4
+    ac, as_, ea, wc, ws, ew = quantized_pair(oracle_mod, M, N, K, 11)
+    t = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in (ac, as_, wc, ws)]
+    big = torch.full((M + 3, ldc), 7.0, dtype=torch.float32, device="cuda")
+    if4.gemm(t[0], t[1], ea, t[2], t[3], ew, out=big[:M, :N])
+    torch.cuda.synchronize()
+    assert bool((big[M:] == 7.0).all()), "a store landed in a row past M"
+    assert bool((big[:M, N:] == 7.0).all()), "a store landed in a column past N"
+    got = big[:M, :N].cpu().numpy()
+    ref = oracle_mod.gemm_sample_f64(ac, as_, ea, wc, ws, ew)
+    err = rel_fro(got, ref)
+    print(f"    rel fro {err:.3e}", flush=True)
+    assert err <= TOL
+
+
 # (a_exp, w_exp) pairs and the power of two the operands are scaled by so
 # that every exact result is a normal fp32 number: the sums of products lie in
 # [2^-18, 2^23] times the operand scale squared, and C = sum * 2^(a_exp + w_exp)
