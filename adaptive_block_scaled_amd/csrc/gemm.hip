@@ -487,7 +487,24 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     lw = w_scale(raw[1], win[0], 1, 1, 0, 0);
     lds_barrier();
 
-    const int w_off = lane * 16;  // fragment (block j, step t) at j * FRAG_BLOCK + t * FRAG_STEP
+    // Block order per wave: the wave's logical W block j = 2m + b is the tile's
+    // block 2 (m ^ wave) + b, so that its first two blocks are the two it
+    // decodes itself (tile rows 64 wave .. 64 wave + 63).  Those it can read
+    // for the next slab before the barrier (a wave's own LDS writes and
+    // reads complete in order), and step 0 of each slab starts with the four
+    // MFMAs on them while the other six fragments arrive.
+    // fragment (logical block 2m + b, step t) at fb[m] + b * FRAG_BLOCK + t * FRAG_STEP
+    int fb[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) fb[m] = lane * 16 + 2 * (m ^ wave) * FRAG_BLOCK;
+    auto frag = [&](const uint8_t* b, int j, int t) {
+        return *reinterpret_cast<const half8*>(b + fb[j >> 1] + (j & 1) * FRAG_BLOCK +
+                                               t * FRAG_STEP);
+    };
+    half8 bv[2][8];  // fragments of even / odd steps
+    // slab 0's first two (own) fragments
+    bv[0][0] = frag(smem, 0, 0);
+    bv[0][1] = frag(smem, 1, 0);
 
     // One slab s = s0 + U (s0 a multiple of 4): MFMAs of slab s from buffer
     // U%2 while slab s+1 (register set (U+1)%2) is decoded into the other
@@ -509,10 +526,9 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
 
         // step 0's fragments first, all eight before any MFMA, so that only
         // the first read's latency is exposed after the barrier
-        half8 bv[2][8];  // fragments of even / odd steps
+        // (logical blocks 0 and 1 were read before the barrier)
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            bv[0][j] = *reinterpret_cast<const half8*>(buf + w_off + j * FRAG_BLOCK);
+        for (int j = 2; j < 8; j++) bv[0][j] = frag(buf, j, 0);
         load_codes(raw[P], (int64_t)s + 2);
 #pragma unroll
         for (int t = 0; t < kGroups; t++) {
@@ -539,17 +555,19 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
             if (t + 1 < kGroups) {
 #pragma unroll
                 for (int j = 0; j < 8; j++)
-                    bv[(t + 1) & 1][j] = *reinterpret_cast<const half8*>(
-                        buf + w_off + j * FRAG_BLOCK + (t + 1) * FRAG_STEP);
+                    bv[(t + 1) & 1][j] = frag(buf, j, t + 1);
             }
             half8 w1;
-            // sub-blocks: (A block 0, W 0..3), (1, 0..3), (0, 4..7), (1, 4..7)
+            // sub-blocks: (A block 0, W 0..3), (1, 0..3), (0, 4..7), (1, 4..7);
+            // in step 0, W blocks in pairs, (0, 0..1) (1, 0..1), (0, 2..3)
+            // (1, 2..3), ..., so that the four MFMAs on the wave's own blocks
+            // come first
 #pragma unroll
             for (int sb = 0; sb < 4; sb++) {
-                const int i = sb & 1;  // A block of this sub-block's MFMAs
 #pragma unroll
                 for (int jj = 0; jj < 4; jj++) {
-                    const int j = 4 * (sb >> 1) + jj;
+                    const int i = t == 0 ? (jj >> 1) : (sb & 1);  // A block
+                    const int j = t == 0 ? 2 * sb + (jj & 1) : 4 * (sb >> 1) + jj;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][t], bv[t & 1][j],
                                                                        acc[i][j], 0, 0, 0);
                 }
@@ -561,6 +579,12 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                     w1 = w_decode_store0(x, sw, k, gg, nbuf);
                 } else if (sb == 2) {
                     w_store1(w1, k, gg, nbuf);
+                    if (t == kGroups - 1) {
+                        // the next slab's first two fragments: this wave's
+                        // own blocks, all written by now (in program order)
+                        bv[0][0] = frag(nbuf, 0, 0);
+                        bv[0][1] = frag(nbuf, 1, 0);
+                    }
                 } else if (sb == 3 && t == 1) {
                     a_decode(x.aword(0, 0), x.aword(0, 1), sa, 0, 0);  // slab s+1
                 } else if (sb == 3 && t == 3) {
@@ -630,7 +654,8 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            if (n0 + 32 * j + cl < N) {
+            const int pj = 2 * ((j >> 1) ^ wv) + (j & 1);  // the tile's column block
+            if (n0 + 32 * pj + cl < N) {
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -638,7 +663,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
                         const int so = (64 * wv + 32 * i + 8 * (r >> 2) + (r & 3)) * (int)ld4;
                         __builtin_amdgcn_raw_buffer_store_b32(
                             __float_as_uint(__builtin_amdgcn_ldexpf(acc[i][j][r], out_exp)), crs,
-                            vo + j * 128, so, kNonTemporal);
+                            vo, so + pj * 128, kNonTemporal);
                     }
             }
         }
@@ -648,7 +673,7 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            const int64_t col = n0 + j * 32 + (lane & 31);
+            const int64_t col = n0 + (2 * ((j >> 1) ^ wave) + (j & 1)) * 32 + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * eh + (r & 3);
