@@ -634,9 +634,13 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     // stores: nothing here reads it again, and dirty C lines left in the
     // caches slow whatever kernel runs next (a 470 MB quantize launched after
     // this GEMM took 125 us instead of 101 us)
-    // (the lane half recomputed from the lane id, so that nothing computed
-    // before the K loop has to stay live across it)
-    const int eh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
+    // (the lane id recomputed, and the wave index read back from the
+    // fragment base of logical block 0, lane * 16 + wave * 2 FRAG_BLOCK, so
+    // that nothing computed before the K loop has to stay live across it
+    // for the epilogue alone)
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int eh = ln >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(fb[0] / (2 * FRAG_BLOCK));
     // Stores go through a buffer resource based at the tile's first output
     // and sized to the tile's rows that exist (a store to a row past M falls
     // outside it and is dropped by the hardware): the lane's column and row
@@ -649,9 +653,8 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         const int rows_valid = (int)(M - m0 < BM ? M - m0 : BM);
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(c + m0 * ldc + n0), 0, (int)((uint32_t)rows_valid * ld4), kRawBufferFlags);
-        const int cl = lane & 31;
+        const int cl = ln & 31;
         const uint32_t vo = (uint32_t)cl * 4 + (uint32_t)(4 * eh) * ld4;
-        const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int pj = 2 * ((j >> 1) ^ wv) + (j & 1);  // the tile's column block
@@ -673,10 +676,10 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            const int64_t col = n0 + (2 * ((j >> 1) ^ wave) + (j & 1)) * 32 + (lane & 31);
+            const int64_t col = n0 + (2 * ((j >> 1) ^ wv) + (j & 1)) * 32 + (ln & 31);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + 64 * wave + 32 * i + 8 * (r >> 2) + 4 * eh + (r & 3);
+                const int64_t row = m0 + 64 * wv + 32 * i + 8 * (r >> 2) + 4 * eh + (r & 3);
                 if (row < M && col < N)
                     __builtin_nontemporal_store(__builtin_amdgcn_ldexpf(acc[i][j][r], out_exp),
                                                 &c[row * ldc + col]);
