@@ -286,10 +286,14 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int u) {
 // codes of slab s+2 into the register set that slab s used; scales arrive a
 // window ahead.  The slab loop is unrolled by the 4-slab window so that all
 // register sets are fixed and no loaded value is copied (a copy would wait
-// for its load).  One LDS-only barrier per slab, after which the eight W
-// fragments of the slab's first step are read before any MFMA is issued.
+// for its load).  One LDS-only barrier per slab.  Each wave numbers the W
+// blocks in its own order, its own two (the ones it decodes) first: their
+// first-step fragments for the next slab are read before the barrier, the
+// other six right after it, before any MFMA is issued, and step 0 opens with
+// the four MFMAs on the own blocks while those six arrive.
 // Within a slab, each MFMA step runs four sub-blocks of four MFMAs: (A block
-// 0, W blocks 0..3), (1, 0..3), (0, 4..7), (1, 4..7); the eight W fragments
+// 0, W blocks 0..3), (1, 0..3), (0, 4..7), (1, 4..7) -- in step 0 the W
+// blocks go in pairs, (0, 0..1) (1, 0..1), (0, 2..3) (1, 2..3), ...; the eight W fragments
 // of the next step are read into a second register set at the start of the
 // step, a whole step before their use.  Every step decodes two groups: one
 // of W (row t/2, group 2q + t%2 of the next slab, stored in sub-blocks 1
@@ -524,9 +528,8 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         constexpr int US2 = (U + 2) % kWin;
         const SlabCodes<kWide>& x = raw[Q];
 
-        // step 0's fragments first, all eight before any MFMA, so that only
-        // the first read's latency is exposed after the barrier
-        // (logical blocks 0 and 1 were read before the barrier)
+        // step 0's other six fragments (logical blocks 2..7) before any MFMA;
+        // blocks 0 and 1, the wave's own, were read before the barrier
 #pragma unroll
         for (int j = 2; j < 8; j++) bv[0][j] = frag(buf, j, 0);
         load_codes(raw[P], (int64_t)s + 2);
@@ -626,7 +629,8 @@ gemm_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_s
         }
     }
 
-    // epilogue: lane holds column lane%32 of each 32x32 block, rows
+    // epilogue: lane holds column lane%32 of each 32x32 block (logical block
+    // 2m + b is the tile's column block 2 (m ^ wave) + b), rows
     // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.  Each sum is
     // scaled by 2^out_exp with one v_ldexp_f32 (a single rounding, and only
     // where the result leaves the fp32 range: out_exp spans [-110, 146], more
