@@ -108,6 +108,36 @@ def test_every_bf16_amax_sets_the_scale(oracle_mod):
         check(oracle_mod, x2.reshape(-1, 64), "bf16", e, label=f"amax+tail E={e}")
 
 
+@pytest.mark.parametrize("e", [0, -3, 5])
+def test_int4_clamp_only_where_needed(oracle_mod, e):
+    """The row kernel runs the INT4 loop without its clamp in waves whose 64
+    groups all have ordinary scales.  Groups whose largest element sits at
+    the bound of that elision (a/6 = 2^k * 1.0625 exactly, a tie that rounds
+    the scale down to 2^k, so 7a/(6s) = 7.4375) fill every wave; in every
+    other wave one group has an E4M3 subnormal scale (a = 2^-6 * 2^e: 7a/(6s)
+    = 9.33, which only the clamp brings back to 7) or one a saturating scale
+    (a/6 = 600 * 2^e).  Codes and scale bytes must match the oracle in
+    every wave, adaptively and with INT4 forced (where a missing clamp would
+    show in the codes of the groups that need it whatever the selection)."""
+    rng = np.random.default_rng(11)
+    waves, gpw = 96, 64
+    k = rng.integers(-4, 6, waves * gpw)
+    amax = (6.375 * 2.0 ** k).astype(np.float32)  # 6 * 1.0625 * 2^k, exact in bf16
+    x = np.empty((waves * gpw, 16), np.float32)
+    x[:, 0] = amax
+    tail = rng.uniform(-1, 1, (waves * gpw, 15)) * amax[:, None]
+    x[:, 1:] = wl.to_bf16_f32(tail.astype(np.float32))
+    for w in range(1, waves, 2):
+        g = w * gpw + int(rng.integers(0, gpw))
+        big = 2.0 ** -6 if w % 4 == 1 else 3600.0
+        x[g, 0] = big
+        x[g, 1:] = wl.to_bf16_f32((rng.uniform(0.9, 1.0, 15) * big).astype(np.float32))
+    x = (x * np.float32(2.0 ** e)).astype(np.float32)
+    for mode in (0, 2):
+        check(oracle_mod, x.reshape(-1, 64 * 16), "bf16", e, mode,
+              label=f"clamp elision E={e}")
+
+
 def test_exhaustive_element_codes(oracle_mod):
     """Every (bf16 |x| <= 6 s', E4M3 scale s') pair: groups [6 s', x, ...]
     fix the scale at s', so each element's FP4 and INT4 codes and both error
