@@ -265,3 +265,31 @@ def test_exhaustive_bf16_element_codes(oracle_mod, bits):
         c, s_ = check_q(oracle_mod, xe, bits, "bf16", e, label=f"exhaustive E={e}")
         sc_seen = np.unique(s_.cpu().numpy() & 0x7F)
         assert sc_seen.size >= 126
+
+
+@pytest.mark.parametrize("e", [0, -3, 5])
+def test_if3_int_clamp_only_where_needed(oracle_mod, e):
+    """IF3 runs its INT3 loop without the clamp in waves whose 64 groups all
+    have ordinary scales.  Groups at that elision's bound (a/4 = 2^k * 1.0625
+    exactly: the scale rounds down to 2^k and 3a/(4s) = 3.1875) fill every
+    wave; every other wave also holds one group with an E4M3 subnormal scale
+    (a = 5 * 2^-9 * 2^e: 3a/(4s) = 3.75) or one at the 448 code (a = 2304 *
+    2^e: 3.86), which only the clamp brings back to 3.  Adaptive and with
+    INT3 forced."""
+    rng = np.random.default_rng(12)
+    waves, gpw = 96, 64
+    k = rng.integers(-4, 6, waves * gpw)
+    amax = (4.25 * 2.0 ** k).astype(np.float32)  # 4 * 1.0625 * 2^k, exact in bf16
+    x = np.empty((waves * gpw, 16), np.float32)
+    x[:, 0] = amax
+    tail = rng.uniform(-1, 1, (waves * gpw, 15)) * amax[:, None]
+    x[:, 1:] = wl.to_bf16_f32(tail.astype(np.float32))
+    for w in range(1, waves, 2):
+        g = w * gpw + int(rng.integers(0, gpw))
+        big = 5 * 2.0 ** -9 if w % 4 == 1 else 2304.0
+        x[g, 0] = big
+        x[g, 1:] = wl.to_bf16_f32((rng.uniform(0.9, 1.0, 15) * big).astype(np.float32))
+    x = (x * np.float32(2.0 ** e)).astype(np.float32)
+    for mode in (0, 2):
+        check_q(oracle_mod, x.reshape(-1, 64 * 16), 3, "bf16", e, mode,
+                label=f"IF3 clamp elision E={e}")
